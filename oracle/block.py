@@ -1,0 +1,208 @@
+"""NumPy float64 oracle of the unsharded block (test infrastructure only).
+
+Notation follows the pages: X is the activation (tokens x h), W1/A the first
+MLP weight, W2/B the second, H = GELU(X W1) the hidden activation, Y the
+block output.  Weights are [in x out] and used as X @ W (the "张量并行" and
+"Infra: Tensor Parallel" pages write X W; the nn.Linear [out x in] layout of
+the "Megatron-LM 实战 04" code is the transpose of the same map).
+
+Every input is cast to float64 first; inputs are expected to hold exactly the
+values the device consumed (bf16-rounded where the workload is bf16).
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf
+
+_SQRT2 = np.sqrt(2.0)
+_INV_SQRT_2PI = 1.0 / np.sqrt(2.0 * np.pi)
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Activations
+# ---------------------------------------------------------------------------
+def gelu(z):
+    """Exact (erf) GELU: z * Phi(z) = z * 1/2 * [1 + erf(z / sqrt 2)].
+
+    "张量并行", section MLP 层的并行化 (the GELU formula under Row -> Column)."""
+    z = _f64(z)
+    return z * 0.5 * (1.0 + erf(z / _SQRT2))
+
+
+def gelu_grad(z):
+    """d/dz [z Phi(z)] = Phi(z) + z phi(z), phi the standard normal density.
+    (Chain rule on the GELU definition above; the pages do not print it.)"""
+    z = _f64(z)
+    return 0.5 * (1.0 + erf(z / _SQRT2)) + z * _INV_SQRT_2PI * np.exp(-0.5 * z * z)
+
+
+def _sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def silu(z):
+    """SiLU(z) = z * sigmoid(z), the gate of the SwiGLU FFN whose W_gate and
+    W_up are column-split (parallelism survey post, section 1 Tensor
+    Parallelism); standard definition, not printed on the pages."""
+    z = _f64(z)
+    return z * _sigmoid(z)
+
+
+def silu_grad(z):
+    """d/dz [z sigmoid(z)] = sigmoid(z) * (1 + z (1 - sigmoid(z)))."""
+    z = _f64(z)
+    s = _sigmoid(z)
+    return s * (1.0 + z * (1.0 - s))
+
+
+def softmax_rows(S):
+    """Row softmax, max-subtracted for range (exact up to rounding)."""
+    S = _f64(S)
+    m = np.max(S, axis=-1, keepdims=True)
+    e = np.exp(S - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# Linear pieces
+# ---------------------------------------------------------------------------
+def linear(X, W, b=None):
+    """Y = X W (+ b).  Column-linear shard i is the same map with W_i, the
+    i-th column block (Infra: Tensor Parallel, Column-wise TP equation)."""
+    Y = _f64(X) @ _f64(W)
+    if b is not None:
+        Y = Y + _f64(b).reshape(1, -1)
+    return Y
+
+
+def row_partial(Xi, Wi):
+    """P_i = X_i W_i: one term of the row-wise sum  X W = sum_i X_i W_i
+    ("张量并行", section 两个矩阵相乘, first step; Infra: Tensor Parallel,
+    Row-wise TP equation).  No bias: the row bias is added once, after the
+    sum, since sum_i (P_i + b) = X W + n b."""
+    return _f64(Xi) @ _f64(Wi)
+
+
+def shard_sum(partials, bias=None):
+    """Y = sum_i P_i (+ b once): what the all-reduce of the row-parallel layer
+    delivers ("张量并行", 行并行 / MLP 层的并行化: g's forward all-reduce)."""
+    acc = np.zeros_like(_f64(partials[0]))
+    for P in partials:
+        acc = acc + _f64(P)
+    if bias is not None:
+        acc = acc + _f64(bias).reshape(1, -1)
+    return acc
+
+
+# ---------------------------------------------------------------------------
+# MLP blocks
+# ---------------------------------------------------------------------------
+def mlp_gelu(X, W1, W2, b1=None, b2=None):
+    """Y = GELU(X W1 + b1) W2 + b2.
+
+    The Megatron MLP of "张量并行" (MLP 层的并行化, the A-column / B-row
+    formula) and of "Infra: Tensor Parallel" (MLP section):
+        Y = GELU(X [A_1 A_2]) [B_1; B_2] = sum_i GELU(X A_i) B_i.
+    Returns dict(Z=pre-activation, H=hidden, Y=output)."""
+    Z = linear(X, W1, b1)
+    H = gelu(Z)
+    Y = H @ _f64(W2)
+    if b2 is not None:
+        Y = Y + _f64(b2).reshape(1, -1)
+    return {"Z": Z, "H": H, "Y": Y}
+
+
+def mlp_swiglu(X, Wg, Wu, Wd):
+    """Y = (SiLU(X Wg) * (X Wu)) Wd, '*' elementwise.  W_gate and W_up are
+    column-split, the second layer row-split (parallelism survey post,
+    section 1 Tensor Parallelism)."""
+    Zg = linear(X, Wg)
+    Zu = linear(X, Wu)
+    H = silu(Zg) * Zu
+    return {"Zg": Zg, "Zu": Zu, "H": H, "Y": H @ _f64(Wd)}
+
+
+def mlp_gelu_backward(X, W1, W2, dY, b1=None):
+    """Gradients of L = <Y, dY> for Y = GELU(X W1 + b1) W2.
+
+    Row-wise layer (Infra: Tensor Parallel, Row-wise TP backward):
+        dW2 = H^T dY,  dH = dY W2^T.
+    Elementwise activation (chain rule): dZ = dH * GELU'(Z), db1 = sum_rows dZ.
+    Column-wise layer (Infra: Tensor Parallel, Column-wise TP backward):
+        dW1 = X^T dZ,  dX = dZ W1^T  (= sum_i dZ_i W1_i^T over column shards).
+    """
+    X, W1, W2, dY = _f64(X), _f64(W1), _f64(W2), _f64(dY)
+    Z = linear(X, W1, b1)
+    H = gelu(Z)
+    dW2 = H.T @ dY
+    dH = dY @ W2.T
+    dZ = dH * gelu_grad(Z)
+    return {"Z": Z, "H": H, "dH": dH, "dZ": dZ, "dW2": dW2, "dW1": X.T @ dZ,
+            "db1": dZ.sum(axis=0), "dX": dZ @ W1.T}
+
+
+def mlp_swiglu_backward(X, Wg, Wu, Wd, dY):
+    """Gradients of L = <Y, dY> for Y = (SiLU(X Wg) * X Wu) Wd.
+
+    dWd = H^T dY, dH = dY Wd^T (row-wise layer);
+    dZu = dH * SiLU(Zg), dZg = dH * Zu * SiLU'(Zg) (chain rule);
+    dWg = X^T dZg, dWu = X^T dZu, dX = dZg Wg^T + dZu Wu^T (column-wise)."""
+    X, Wg, Wu, Wd, dY = _f64(X), _f64(Wg), _f64(Wu), _f64(Wd), _f64(dY)
+    Zg = X @ Wg
+    Zu = X @ Wu
+    H = silu(Zg) * Zu
+    dH = dY @ Wd.T
+    dZu = dH * silu(Zg)
+    dZg = dH * Zu * silu_grad(Zg)
+    return {"Zg": Zg, "Zu": Zu, "H": H, "dH": dH, "dZg": dZg, "dZu": dZu,
+            "dWd": H.T @ dY, "dWg": X.T @ dZg, "dWu": X.T @ dZu,
+            "dX": dZg @ Wg.T + dZu @ Wu.T}
+
+
+# ---------------------------------------------------------------------------
+# Multi-head attention
+# ---------------------------------------------------------------------------
+def attention_heads(Q, K, V, causal):
+    """O = softmax(Q K^T / sqrt(d) [+ causal mask]) V for ONE head of one
+    sequence.  Q, K, V: [s, d].  Scores with key j > query i are excluded
+    when causal (the diagonal is always kept, so no row is empty).
+
+    Scaled dot-product as in "Megatron-LM 实战 04" (TPAttention.forward);
+    causal masking is the workload's choice (decoder self-attention)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    d = Q.shape[1]
+    S = (Q @ K.T) / np.sqrt(d)
+    if causal:
+        s = S.shape[0]
+        mask = np.triu(np.ones((s, S.shape[1]), dtype=bool), k=1)
+        S = np.where(mask, -np.inf, S)
+    P = softmax_rows(S)
+    return P @ V
+
+
+def mha(X, Wq, Wk, Wv, Wo, heads, b, s, causal=True):
+    """Unsharded multi-head attention block output Y and concatenated head
+    outputs O (token-major [b*s, heads*d]).
+
+    Head t uses columns t*d .. (t+1)*d - 1 of Wq/Wk/Wv with d = h / heads
+    ("张量并行", Multi-Head Attention 的并行化: k_dim = v_dim = h // heads);
+    O_t = Attention(X Wq^(t), X Wk^(t), X Wv^(t)) and Y = [O_1 ... O_H] Wo
+    (Infra: Tensor Parallel, MHA equation).  Batch elements are independent.
+    """
+    X, Wq, Wk, Wv, Wo = _f64(X), _f64(Wq), _f64(Wk), _f64(Wv), _f64(Wo)
+    h = X.shape[1]
+    if h % heads:
+        raise ValueError("hidden size must be a multiple of the head count")
+    d = h // heads
+    Q, K, V = X @ Wq, X @ Wk, X @ Wv
+    O = np.zeros((b * s, Wq.shape[1]), dtype=np.float64)
+    for bi in range(b):
+        r = slice(bi * s, (bi + 1) * s)
+        for t in range(Wq.shape[1] // d):
+            c = slice(t * d, (t + 1) * d)
+            O[r, c] = attention_heads(Q[r, c], K[r, c], V[r, c], causal)
+    return {"Q": Q, "K": K, "V": V, "O": O, "Y": O @ Wo}
