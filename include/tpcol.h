@@ -1,0 +1,215 @@
+/*
+ * tpcol.h -- C ABI of the MI355X (gfx950) tensor-parallel shard library.
+ *
+ * The library computes ONE tensor-parallel shard's share of a transformer
+ * block on one GPU: the column-parallel GEMM with a fused activation
+ * epilogue, head-local attention, the row-parallel GEMM that yields a
+ * partial sum, the sum of the N partials (standing in for the all-reduce),
+ * and the MLP backward.  Shard i of N is the i-th contiguous block:
+ *   column shard  W_i = W[:, i*w : (i+1)*w]   (output dimension split)
+ *   row shard     W_i = W[i*w : (i+1)*w, :]   (input dimension split)
+ * following "张量并行" (section 并行化矩阵乘法运算: column-linear and
+ * row-linear sharding; section MLP 层的并行化: A column-split, B row-split)
+ * and "Infra: Tensor Parallel" (Column-wise TP / Row-wise TP equations).
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major; ld* is the row stride in ELEMENTS (>= width).
+ *   - Weights are [in x out] and used as X @ W (the pages' X W notation).
+ *   - dtype TP_F32: every operand float32.  TP_BF16: inputs, weights and the
+ *     activation outputs are bfloat16 (raw 16-bit patterns); accumulation is
+ *     always float32; partial sums P and all gradients are float32.
+ *   - Pointers are DEVICE pointers unless stated otherwise, must be 16-byte
+ *     aligned, and ld * element size must be a multiple of 16 bytes.  The
+ *     contiguous (last) dimension of every matrix must be a multiple of the
+ *     16-byte vector (8 elements for bf16, 4 for fp32).  Token counts
+ *     (M, b*s) may be anything >= 0; M == 0 is a no-op returning TP_OK
+ *     (the backward then writes zero weight gradients), and the pointers
+ *     of empty matrices may be NULL.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous: they validate on the host, enqueue kernels and return.
+ *     Kernel faults surface at the caller's next synchronisation.
+ *   - The library never allocates device memory.  Scratch space comes from
+ *     the caller's workspace (ws, ws_bytes); query its size with the
+ *     matching *_workspace() function.  A workspace must not be used by two
+ *     calls that can run at the same time.
+ *   - Validation happens before any launch; on error nothing is enqueued,
+ *     outputs are untouched and a detail string is kept for tp_last_error().
+ *   - Operands must not alias outputs.
+ */
+#ifndef TPCOL_H
+#define TPCOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TP_OK = 0,
+    TP_ERR_ARG = -1,        /* NULL required pointer, bad enum, bad count        */
+    TP_ERR_SHAPE = -2,      /* non-positive size, ld < width, indivisible split  */
+    TP_ERR_ALIGN = -3,      /* pointer / ld / width not 16-byte vectorisable     */
+    TP_ERR_DTYPE = -4,      /* unsupported dtype for this call                   */
+    TP_ERR_WORKSPACE = -5,  /* workspace NULL or smaller than required           */
+    TP_ERR_HIP = -6         /* a HIP runtime call or kernel launch failed        */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum {
+    TP_ACT_NONE = 0,        /* identity (e.g. the QKV projection)                */
+    TP_ACT_GELU_ERF = 1,    /* exact GELU  z * Phi(z)                            */
+    TP_ACT_SWIGLU = 2       /* SiLU(X Wg) * (X Wu): needs the second weight Wup  */
+} tp_act;
+
+/*
+ * Column-parallel linear with fused activation:
+ *     H_i = act(X @ W_i + bias_i)            (TP_ACT_NONE / TP_ACT_GELU_ERF)
+ *     H_i = SiLU(X @ W_i) * (X @ Wup_i)      (TP_ACT_SWIGLU; bias must be NULL)
+ * X is replicated on every shard (no communication before the layer);
+ * W_i is the i-th column block.  The activation is column-separable, so it is
+ * applied per shard ("张量并行", MLP 层的并行化: GELU([Y1,Y2]) =
+ * [GELU(Y1), GELU(Y2)]; "Infra: Tensor Parallel", Column-wise TP).  The
+ * pre-activation is never written to memory.
+ *   X    [M x K]   ldx         dtype
+ *   W    [K x Ni]  ldw         dtype   (W_gate for SwiGLU)
+ *   Wup  [K x Ni]  ldwu        dtype   (SwiGLU only, else NULL)
+ *   bias [Ni]                  dtype   (optional, NULL for none)
+ *   H    [M x Ni]  ldh         dtype   (output)
+ * M <= the GEMV threshold (16 by default) selects the weight-streaming decode
+ * path, which needs tp_col_linear_gelu_workspace() bytes of ws (256-byte
+ * aligned) when K > 512.  Its first 64 KiB hold split-K arrival counters:
+ * they must be zero before the first use of the buffer, every completed call
+ * leaves them zero again, and buffers may be shared by calls of any shape
+ * (not concurrently).  Larger M needs no workspace (ws may be NULL).
+ */
+int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni,
+                       const void *X, int64_t ldx,
+                       const void *W, int64_t ldw,
+                       const void *Wup, int64_t ldwu,
+                       const void *bias,
+                       void *H, int64_t ldh,
+                       void *ws, size_t ws_bytes, void *stream);
+size_t tp_col_linear_gelu_workspace(int dtype, int act, int64_t M, int64_t K, int64_t Ni);
+
+/*
+ * Row-parallel linear, this shard's partial sum (no bias, no reduction):
+ *     P_i = X_i @ W_i
+ * X_i is this shard's slice of the input's last dimension (H_i or O_i), W_i
+ * the i-th row block ("张量并行", 两个矩阵相乘: X A = sum_i X_i A_i;
+ * "Infra: Tensor Parallel", Row-wise TP).  The row bias belongs after the
+ * sum (tp_shard_sum), since adding it per shard would count it N times.
+ *   Xi [M x Ki] ldx dtype ; Wi [Ki x N] ldw dtype ; P [M x N] ldp float32.
+ * Workspace rules as for tp_col_linear_gelu (needed only for M <= threshold).
+ */
+int tp_row_linear_partial(int dtype, int64_t M, int64_t Ki, int64_t N,
+                          const void *Xi, int64_t ldx,
+                          const void *Wi, int64_t ldw,
+                          float *P, int64_t ldp,
+                          void *ws, size_t ws_bytes, void *stream);
+size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t N);
+
+/*
+ * Head-sharded self-attention block, this shard's partial output:
+ *     [Q | K | V] = X @ Wqkv_i            (heads_local heads, each d wide)
+ *     O_t = softmax(Q_t K_t^T / sqrt(d) [+ causal mask]) V_t   per head t
+ *     P_i = [O_1 ... O_heads_local] @ Wo_i
+ * The local heads feed the local row block of Wo directly: no gather of the
+ * heads is needed ("Infra: Tensor Parallel", MHA: Wo row-wise, heads
+ * column-wise; "张量并行", Multi-Head Attention 的并行化; parallelism survey
+ * post, section 1 Tensor Parallelism).  Packing of Wqkv_i columns: Q heads,
+ * then K heads, then V heads, head t at offset t*d inside each block
+ * ("Megatron-LM 实战 04", TPAttention: qkv reshaped to (3, heads, d)).
+ * Causal: key j is visible to query i iff j <= i (within one sequence).
+ *   X    [b*s x h]                      ldx    bf16 (token-major, batch-major)
+ *   Wqkv [h x 3*heads_local*d]          ldwqkv bf16
+ *   Wo   [heads_local*d x h]            ldwo   bf16
+ *   P    [b*s x h]                      ldp    float32 (output)
+ *   ws   tp_attn_heads_shard_workspace() bytes: QKV_i [b*s x 3*hl*d] then
+ *        O_i [b*s x hl*d], both bf16 row-major, readable after the call.
+ * Only TP_BF16 and d == 128 are supported (TP_ERR_DTYPE / TP_ERR_SHAPE).
+ */
+int tp_attn_heads_shard(int dtype, int64_t b, int64_t s, int64_t h,
+                        int64_t heads_local, int64_t d, int causal,
+                        const void *X, int64_t ldx,
+                        const void *Wqkv, int64_t ldwqkv,
+                        const void *Wo, int64_t ldwo,
+                        float *P, int64_t ldp,
+                        void *ws, size_t ws_bytes, void *stream);
+size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s,
+                                     int64_t heads_local, int64_t d);
+
+/*
+ * Sum of the N shard partials, added in shard order in float32, plus an
+ * optional bias added once:
+ *     Y = sum_{i<n} P_i (+ bias)
+ * It stands in for the row-parallel layer's all-reduce (g's forward;
+ * "张量并行", 行并行 and MLP 层的并行化) and for the column layer's backward
+ * all-reduce of dX (f's backward) when all partials live in one GPU.
+ *   partials  HOST array of n device pointers, each [M x N] float32, ldp
+ *   bias      [N] float32 or NULL
+ *   Y         [M x N] ldy, out_dtype (TP_F32 or TP_BF16, RNE rounding)
+ * 1 <= n <= 64.  Y may alias partials[0] when out_dtype == TP_F32 and
+ * ldy == ldp.
+ */
+int tp_shard_sum(int out_dtype, int64_t M, int64_t N, int n,
+                 const float *const *partials, int64_t ldp,
+                 const float *bias, void *Y, int64_t ldy, void *stream);
+
+/*
+ * MLP shard backward given dY (broadcast to every shard):
+ *   row layer    dW2_i = H_i^T dY,  dH_i = dY W2_i^T
+ *   activation   dZ_i = dH_i * GELU'(Z_i)          (GELU; Z_i recomputed)
+ *                dZu = dH * SiLU(Zg), dZg = dH * Zu * SiLU'(Zg)   (SwiGLU)
+ *   column layer dW1_i = X^T dZ_i,  db1_i = sum over tokens of dZ_i,
+ *                dX_i = dZ_i W1_i^T (SwiGLU: dZg Wg_i^T + dZu Wu_i^T)
+ * ("Infra: Tensor Parallel", Column-wise and Row-wise TP backward equations;
+ * "张量并行", 行并行 backward of g and MLP 层的并行化 backward of f.)
+ * dX_i is this shard's partial of dX = sum_i dX_i; sum them with
+ * tp_shard_sum (f's backward all-reduce).
+ *   X  [M x K] ldx, W1 [K x Ni] ldw1 (W_gate for SwiGLU), Wup [K x Ni] ldwu
+ *   (SwiGLU else NULL), b1 [Ni] (GELU only, optional), W2 [Ni x K] ldw2,
+ *   dY [M x K] lddy: all dtype.
+ *   Outputs (float32, dense): dW1 [K x Ni], dWup [K x Ni] (SwiGLU else NULL),
+ *   dW2 [Ni x K], db1 [Ni] (optional; GELU only), dXi [M x K] ldd x.
+ *   ws: tp_mlp_shard_backward_workspace() bytes; holds dH_i, H_i and dZ_i
+ *   ([M x Ni] each, dtype; dZg and dZu for SwiGLU).
+ */
+int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni,
+                          const void *X, int64_t ldx,
+                          const void *W1, int64_t ldw1,
+                          const void *Wup, int64_t ldwu,
+                          const void *b1,
+                          const void *W2, int64_t ldw2,
+                          const void *dY, int64_t lddy,
+                          float *dW1, float *dWup, float *dW2, float *db1,
+                          float *dXi, int64_t lddx,
+                          void *ws, size_t ws_bytes, void *stream);
+size_t tp_mlp_shard_backward_workspace(int dtype, int act, int64_t M, int64_t Ni);
+
+/*
+ * Host-only divisibility check of a tensor-parallel split (no GPU use):
+ * ffn % n == 0, heads % n == 0 and h % heads == 0 ("Megatron-LM 实战 04",
+ * TPAttention asserts and 常见问题; "Infra: Tensor Parallel", the head count
+ * must be a multiple of the TP size).  heads == 0 skips the head checks.
+ * Returns TP_OK or TP_ERR_SHAPE.
+ */
+int tp_check_split(int64_t h, int64_t ffn, int64_t heads, int64_t n);
+
+/* Tuning/testing option: token count at or below which the linear calls take
+ * the decode GEMV path (default 16, range 0..16; 0 disables the GEMV path).
+ * Process-wide; returns the previous value, or TP_ERR_ARG if out of range. */
+int tp_set_gemv_max_m(int max_m);
+
+/* Static description of a status code.  Never NULL. */
+const char *tp_status_string(int status);
+
+/* Detail of the last failing call on the calling thread ("" if none). */
+const char *tp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPCOL_H */

@@ -1,0 +1,469 @@
+// C ABI of the tensor-parallel shard library: argument validation, path
+// selection and kernel sequencing.  Declarations and contracts are in
+// include/tpcol.h.  Every check runs before the first launch, so a failing
+// call enqueues nothing.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/tpcol.h"
+#include "kernels.hpp"
+
+using namespace tpcol;
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_gemv_max_m{16};
+
+int fail(int status, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return TP_OK;
+}
+
+size_t esize(int dtype) { return dtype == TP_BF16 ? 2 : 4; }
+
+bool dtype_ok(int dtype) { return dtype == TP_F32 || dtype == TP_BF16; }
+
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;  // kernels index rows/cols with int
+
+// A [rows x cols] row-major matrix with row stride ld elements of size es.
+// An empty matrix (rows == 0) may have a NULL pointer.
+int check_mat(const void *p, int64_t rows, int64_t cols, int64_t ld, size_t es, const char *name,
+              bool required = true) {
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim)
+    return fail(TP_ERR_SHAPE, "%s has an invalid shape %lld x %lld", name, (long long)rows,
+                (long long)cols);
+  if (p == nullptr) {
+    if (required && rows > 0) return fail(TP_ERR_ARG, "%s is NULL", name);
+    return TP_OK;
+  }
+  if (ld < cols)
+    return fail(TP_ERR_SHAPE, "%s: leading dimension %lld < width %lld", name, (long long)ld,
+                (long long)cols);
+  if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0)
+    return fail(TP_ERR_ALIGN, "%s is not 16-byte aligned", name);
+  if (((size_t)ld * es) % 16 != 0)
+    return fail(TP_ERR_ALIGN, "%s: leading dimension %lld is not a multiple of 16 bytes", name,
+                (long long)ld);
+  if (((size_t)cols * es) % 16 != 0)
+    return fail(TP_ERR_ALIGN, "%s: width %lld is not a multiple of %zu elements", name,
+                (long long)cols, 16 / es);
+  return TP_OK;
+}
+
+int check_vec(const void *p, int64_t n, size_t es, const char *name) {
+  if (p == nullptr) return TP_OK;  // optional vectors
+  return check_mat(p, 1, n, n, es, name);
+}
+
+int check_dims(std::initializer_list<int64_t> dims, const char *what) {
+  for (int64_t d : dims)
+    if (d < 0 || d > kMaxDim) return fail(TP_ERR_SHAPE, "%s: dimension %lld out of range", what, (long long)d);
+  return TP_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return TP_OK;
+}
+
+#define TRY(x)               \
+  do {                       \
+    const int _st = (x);     \
+    if (_st != TP_OK) return _st; \
+  } while (0)
+
+bool use_gemv(int dtype, int64_t M) {
+  return dtype == TP_BF16 && M >= 1 && M <= g_gemv_max_m.load(std::memory_order_relaxed);
+}
+
+// Backward workspace layout: dH [M x Ni], H [M x Ni], dZ [M x Ni] (GELU) or
+// [M x 2Ni] = [dZg | dZu] (SwiGLU); each region 256-byte aligned.
+struct BwdWs {
+  size_t dH, H, dZ, total;
+};
+BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
+  const size_t e = esize(dtype);
+  const size_t one = round256((size_t)M * (size_t)Ni * e);
+  BwdWs w;
+  w.dH = 0;
+  w.H = one;
+  w.dZ = 2 * one;
+  w.total = w.dZ + (act == TP_ACT_SWIGLU ? round256((size_t)M * 2 * (size_t)Ni * e) : one);
+  return w;
+}
+
+struct AttnWs {
+  size_t qkv, o, total;
+};
+AttnWs attn_ws(int64_t b, int64_t s, int64_t hl, int64_t d) {
+  const size_t T = (size_t)b * (size_t)s;
+  AttnWs w;
+  w.qkv = 0;
+  w.o = round256(T * 3 * (size_t)hl * (size_t)d * 2);
+  w.total = w.o + round256(T * (size_t)hl * (size_t)d * 2);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tp_status_string(int status) {
+  switch (status) {
+    case TP_OK: return "TP_OK: success";
+    case TP_ERR_ARG: return "TP_ERR_ARG: invalid or missing argument";
+    case TP_ERR_SHAPE: return "TP_ERR_SHAPE: invalid shape or split";
+    case TP_ERR_ALIGN: return "TP_ERR_ALIGN: pointer or stride not 16-byte vectorisable";
+    case TP_ERR_DTYPE: return "TP_ERR_DTYPE: unsupported dtype";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_HIP: return "TP_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *tp_last_error(void) { return g_err; }
+
+int tp_set_gemv_max_m(int max_m) {
+  if (max_m < 0 || max_m > 16) return fail(TP_ERR_ARG, "gemv threshold %d outside 0..16", max_m);
+  return g_gemv_max_m.exchange(max_m);
+}
+
+int tp_check_split(int64_t h, int64_t ffn, int64_t heads, int64_t n) {
+  if (n < 1) return fail(TP_ERR_SHAPE, "shard count %lld < 1", (long long)n);
+  if (h < 1 || ffn < 0 || heads < 0) return fail(TP_ERR_SHAPE, "negative or zero size");
+  if (ffn % n != 0)
+    return fail(TP_ERR_SHAPE, "ffn %lld is not divisible by %lld shards", (long long)ffn, (long long)n);
+  if (heads > 0) {
+    if (h % heads != 0)
+      return fail(TP_ERR_SHAPE, "hidden %lld is not divisible by %lld heads", (long long)h,
+                  (long long)heads);
+    if (heads % n != 0)
+      return fail(TP_ERR_SHAPE, "heads %lld must be a multiple of the shard count %lld",
+                  (long long)heads, (long long)n);
+  }
+  return ok();
+}
+
+size_t tp_col_linear_gelu_workspace(int dtype, int act, int64_t M, int64_t K, int64_t Ni) {
+  if (act != TP_ACT_SWIGLU && use_gemv(dtype, M) && Ni <= gemv_max_n()) return gemv_workspace(K, Ni);
+  return 0;
+}
+
+size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t N) {
+  if (use_gemv(dtype, M) && N <= gemv_max_n()) return gemv_workspace(Ki, N);
+  return 0;
+}
+
+size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
+                                     int64_t d) {
+  (void)dtype;
+  if (b < 0 || s < 0 || heads_local < 0 || d < 0) return 0;
+  return attn_ws(b, s, heads_local, d).total;
+}
+
+size_t tp_mlp_shard_backward_workspace(int dtype, int act, int64_t M, int64_t Ni) {
+  if (M < 0 || Ni < 0) return 0;
+  return bwd_ws(dtype, act, M, Ni).total;
+}
+
+int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
+                       int64_t ldx, const void *W, int64_t ldw, const void *Wup, int64_t ldwu,
+                       const void *bias, void *H, int64_t ldh, void *ws, size_t ws_bytes,
+                       void *stream) {
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU_ERF && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_ARG, "activation %d", act);
+  TRY(check_dims({M, K, Ni}, "tp_col_linear_gelu"));
+  if (K < 1 || Ni < 1) return fail(TP_ERR_SHAPE, "K and Ni must be >= 1");
+  const size_t e = esize(dtype);
+  TRY(check_mat(X, M, K, ldx, e, "X"));
+  TRY(check_mat(W, K, Ni, ldw, e, "W"));
+  TRY(check_mat(H, M, Ni, ldh, e, "H"));
+  if (act == TP_ACT_SWIGLU) {
+    if (Wup == nullptr) return fail(TP_ERR_ARG, "SwiGLU needs Wup");
+    if (bias != nullptr) return fail(TP_ERR_ARG, "SwiGLU takes no bias");
+    TRY(check_mat(Wup, K, Ni, ldwu, e, "Wup"));
+  } else if (Wup != nullptr) {
+    return fail(TP_ERR_ARG, "Wup is only used by SwiGLU");
+  }
+  TRY(check_vec(bias, Ni, e, "bias"));
+  if (M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (act != TP_ACT_SWIGLU && use_gemv(dtype, M) && Ni <= gemv_max_n()) {
+    const size_t need = gemv_workspace(K, Ni);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+      return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+      return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+    GemvArgs g;
+    g.dtype = DT_BF16;
+    g.epi = act == TP_ACT_GELU_ERF ? EPI_GELU : EPI_STORE;
+    g.M = M; g.K = K; g.N = Ni;
+    g.X = X; g.ldx = ldx; g.W = W; g.ldw = ldw; g.bias = bias;
+    g.Y = H; g.ldy = ldh; g.ws = ws; g.ws_bytes = ws_bytes;
+    TRY(hip_status(launch_gemv(g, s), "gemv"));
+    return ok();
+  }
+
+  GemmArgs a;
+  a.dtype = dtype;
+  a.layout = LAY_NN;
+  a.M = M; a.N = Ni; a.K = K;
+  a.A = X; a.lda = ldx;
+  a.B = W; a.ldb = ldw;
+  a.C = H; a.ldc = ldh;
+  if (act == TP_ACT_SWIGLU) {
+    a.dual = true;
+    a.epi = EPI_SWIGLU;
+    a.B2 = Wup; a.ldb2 = ldwu;
+  } else {
+    a.epi = act == TP_ACT_GELU_ERF ? EPI_GELU : EPI_STORE;
+    a.bias = bias;
+  }
+  TRY(hip_status(launch_gemm(a, s), "column GEMM"));
+  return ok();
+}
+
+int tp_row_linear_partial(int dtype, int64_t M, int64_t Ki, int64_t N, const void *Xi, int64_t ldx,
+                          const void *Wi, int64_t ldw, float *P, int64_t ldp, void *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
+  TRY(check_dims({M, Ki, N}, "tp_row_linear_partial"));
+  if (Ki < 1 || N < 1) return fail(TP_ERR_SHAPE, "Ki and N must be >= 1");
+  const size_t e = esize(dtype);
+  TRY(check_mat(Xi, M, Ki, ldx, e, "Xi"));
+  TRY(check_mat(Wi, Ki, N, ldw, e, "Wi"));
+  TRY(check_mat(P, M, N, ldp, 4, "P"));
+  if (M == 0) return ok();
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  if (use_gemv(dtype, M) && N <= gemv_max_n()) {
+    const size_t need = gemv_workspace(Ki, N);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+      return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+      return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+    GemvArgs g;
+    g.dtype = DT_BF16;
+    g.epi = EPI_STORE_F32;
+    g.M = M; g.K = Ki; g.N = N;
+    g.X = Xi; g.ldx = ldx; g.W = Wi; g.ldw = ldw;
+    g.Y = P; g.ldy = ldp; g.ws = ws; g.ws_bytes = ws_bytes;
+    TRY(hip_status(launch_gemv(g, s), "gemv"));
+    return ok();
+  }
+  GemmArgs a;
+  a.dtype = dtype;
+  a.layout = LAY_NN;
+  a.epi = EPI_STORE_F32;
+  a.M = M; a.N = N; a.K = Ki;
+  a.A = Xi; a.lda = ldx;
+  a.B = Wi; a.ldb = ldw;
+  a.C = P; a.ldc = ldp;
+  TRY(hip_status(launch_gemm(a, s), "row GEMM"));
+  return ok();
+}
+
+int tp_attn_heads_shard(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
+                        int64_t d, int causal, const void *X, int64_t ldx, const void *Wqkv,
+                        int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P, int64_t ldp,
+                        void *ws, size_t ws_bytes, void *stream) {
+  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports bf16 only");
+  TRY(check_dims({b, s_len, h, heads_local, d}, "tp_attn_heads_shard"));
+  if (h < 1 || heads_local < 1) return fail(TP_ERR_SHAPE, "h and heads_local must be >= 1");
+  if (d != 128) return fail(TP_ERR_SHAPE, "head dim %lld unsupported (128 only)", (long long)d);
+  const int64_t T = b * s_len;
+  if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
+  const int64_t w = heads_local * d;
+  TRY(check_mat(X, T, h, ldx, 2, "X"));
+  TRY(check_mat(Wqkv, h, 3 * w, ldwqkv, 2, "Wqkv"));
+  TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));
+  TRY(check_mat(P, T, h, ldp, 4, "P"));
+  if (T == 0) return ok();
+  const AttnWs L = attn_ws(b, s_len, heads_local, d);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", L.total, ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  void *qkv = base + L.qkv;
+  void *O = base + L.o;
+
+  GemmArgs q;
+  q.dtype = DT_BF16;
+  q.layout = LAY_NN;
+  q.epi = EPI_STORE;
+  q.M = T; q.N = 3 * w; q.K = h;
+  q.A = X; q.lda = ldx;
+  q.B = Wqkv; q.ldb = ldwqkv;
+  q.C = qkv; q.ldc = 3 * w;
+  TRY(hip_status(launch_gemm(q, st), "QKV GEMM"));
+  TRY(hip_status(launch_flash_attn(qkv, 3 * w, O, w, b, s_len, heads_local, d, causal != 0, st),
+                 "attention"));
+  GemmArgs o;
+  o.dtype = DT_BF16;
+  o.layout = LAY_NN;
+  o.epi = EPI_STORE_F32;
+  o.M = T; o.N = h; o.K = w;
+  o.A = O; o.lda = w;
+  o.B = Wo; o.ldb = ldwo;
+  o.C = P; o.ldc = ldp;
+  TRY(hip_status(launch_gemm(o, st), "output GEMM"));
+  return ok();
+}
+
+int tp_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *partials,
+                 int64_t ldp, const float *bias, void *Y, int64_t ldy, void *stream) {
+  if (!dtype_ok(out_dtype)) return fail(TP_ERR_DTYPE, "dtype %d", out_dtype);
+  if (n < 1 || n > 64) return fail(TP_ERR_ARG, "shard count %d outside 1..64", n);
+  if (partials == nullptr) return fail(TP_ERR_ARG, "partials array is NULL");
+  TRY(check_dims({M, N}, "tp_shard_sum"));
+  if (N < 1) return fail(TP_ERR_SHAPE, "N must be >= 1");
+  for (int i = 0; i < n; ++i) {
+    char name[32];
+    snprintf(name, sizeof(name), "partials[%d]", i);
+    TRY(check_mat(partials[i], M, N, ldp, 4, name));
+  }
+  TRY(check_vec(bias, N, 4, "bias"));
+  TRY(check_mat(Y, M, N, ldy, esize(out_dtype), "Y"));
+  if (M == 0) return ok();
+  TRY(hip_status(launch_shard_sum(out_dtype, M, N, n, partials, ldp, bias, Y, ldy,
+                                  static_cast<hipStream_t>(stream)),
+                 "shard sum"));
+  return ok();
+}
+
+int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
+                          int64_t ldx, const void *W1, int64_t ldw1, const void *Wup, int64_t ldwu,
+                          const void *b1, const void *W2, int64_t ldw2, const void *dY,
+                          int64_t lddy, float *dW1, float *dWup, float *dW2, float *db1,
+                          float *dXi, int64_t lddx, void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
+  if (act != TP_ACT_GELU_ERF && act != TP_ACT_SWIGLU)
+    return fail(TP_ERR_ARG, "backward supports GELU and SwiGLU, got activation %d", act);
+  TRY(check_dims({M, K, Ni}, "tp_mlp_shard_backward"));
+  if (K < 1 || Ni < 1) return fail(TP_ERR_SHAPE, "K and Ni must be >= 1");
+  const size_t e = esize(dtype);
+  const bool swiglu = act == TP_ACT_SWIGLU;
+  TRY(check_mat(X, M, K, ldx, e, "X"));
+  TRY(check_mat(W1, K, Ni, ldw1, e, "W1"));
+  TRY(check_mat(W2, Ni, K, ldw2, e, "W2"));
+  TRY(check_mat(dY, M, K, lddy, e, "dY"));
+  TRY(check_mat(dW1, K, Ni, Ni, 4, "dW1"));
+  TRY(check_mat(dW2, Ni, K, K, 4, "dW2"));
+  TRY(check_mat(dXi, M, K, lddx, 4, "dXi"));
+  if (swiglu) {
+    if (Wup == nullptr || dWup == nullptr) return fail(TP_ERR_ARG, "SwiGLU needs Wup and dWup");
+    if (b1 != nullptr || db1 != nullptr) return fail(TP_ERR_ARG, "SwiGLU takes no bias");
+    TRY(check_mat(Wup, K, Ni, ldwu, e, "Wup"));
+    TRY(check_mat(dWup, K, Ni, Ni, 4, "dWup"));
+  } else {
+    if (Wup != nullptr || dWup != nullptr) return fail(TP_ERR_ARG, "Wup/dWup are SwiGLU only");
+    TRY(check_vec(b1, Ni, e, "b1"));
+    TRY(check_vec(db1, Ni, 4, "db1"));
+  }
+  const BwdWs L = bwd_ws(dtype, act, M, Ni);
+  if (M > 0) {
+    if (ws == nullptr || ws_bytes < L.total)
+      return fail(TP_ERR_WORKSPACE, "backward needs %zu workspace bytes, got %zu", L.total, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+      return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  void *dH = base + L.dH;
+  void *H = base + L.H;
+  void *dZ = base + L.dZ;
+  const int64_t ldz = swiglu ? 2 * Ni : Ni;
+  void *dZu = swiglu ? static_cast<void *>(base + L.dZ + (size_t)Ni * e) : nullptr;
+
+  if (M > 0) {
+    // dH = dY W2^T  (row-parallel layer, input gradient of this shard's slice)
+    GemmArgs a;
+    a.dtype = dtype; a.layout = LAY_NT; a.epi = EPI_STORE;
+    a.M = M; a.N = Ni; a.K = K;
+    a.A = dY; a.lda = lddy;
+    a.B = W2; a.ldb = ldw2;
+    a.C = dH; a.ldc = Ni;
+    TRY(hip_status(launch_gemm(a, s), "dH GEMM"));
+
+    // recompute Z = X W1 (+b1) and apply the activation derivative
+    GemmArgs r;
+    r.dtype = dtype; r.layout = LAY_NN;
+    r.M = M; r.N = Ni; r.K = K;
+    r.A = X; r.lda = ldx;
+    r.B = W1; r.ldb = ldw1;
+    r.D = dH; r.ldd = Ni;
+    r.C = dZ; r.ldc = ldz;
+    r.C2 = H; r.ldc2 = Ni;
+    if (swiglu) {
+      r.dual = true; r.epi = EPI_SWIGLU_BWD;
+      r.B2 = Wup; r.ldb2 = ldwu;
+      r.C3 = dZu; r.ldc3 = ldz;
+    } else {
+      r.epi = EPI_GELU_BWD;
+      r.bias = b1;
+    }
+    TRY(hip_status(launch_gemm(r, s), "recompute GEMM"));
+  }
+
+  // dW2 = H^T dY (row-parallel weight gradient)
+  {
+    GemmArgs w;
+    w.dtype = dtype; w.layout = LAY_TN; w.epi = EPI_STORE_F32;
+    w.M = Ni; w.N = K; w.K = M;
+    w.A = H; w.lda = Ni;
+    w.B = dY; w.ldb = lddy;
+    w.C = dW2; w.ldc = K;
+    TRY(hip_status(launch_gemm(w, s), "dW2 GEMM"));
+  }
+  // dW1 = X^T dZ (column-parallel weight gradient; dWup = X^T dZu)
+  {
+    GemmArgs w;
+    w.dtype = dtype; w.layout = LAY_TN; w.epi = EPI_STORE_F32;
+    w.M = K; w.N = Ni; w.K = M;
+    w.A = X; w.lda = ldx;
+    w.B = dZ; w.ldb = ldz;
+    w.C = dW1; w.ldc = Ni;
+    TRY(hip_status(launch_gemm(w, s), "dW1 GEMM"));
+    if (swiglu) {
+      w.B = dZu;
+      w.C = dWup;
+      TRY(hip_status(launch_gemm(w, s), "dWup GEMM"));
+    }
+  }
+  if (db1 != nullptr) TRY(hip_status(launch_colsum(dtype, M, Ni, dZ, ldz, db1, s), "db1"));
+
+  if (M > 0) {
+    // dX_i = dZ W1^T  (SwiGLU: [dZg | dZu] [Wg | Wu]^T in one K-concatenated pass)
+    GemmArgs x;
+    x.dtype = dtype; x.layout = LAY_NT; x.epi = EPI_STORE_F32;
+    x.M = M; x.N = K; x.K = swiglu ? 2 * Ni : Ni;
+    x.A = dZ; x.lda = ldz;
+    x.B = W1; x.ldb = ldw1;
+    if (swiglu) {
+      x.kcat = true; x.K1 = Ni;
+      x.B2 = Wup; x.ldb2 = ldwu;
+    }
+    x.C = dXi; x.ldc = lddx;
+    TRY(hip_status(launch_gemm(x, s), "dX GEMM"));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Shared device-side helpers for the gfx950 kernels: storage types, bf16
+// conversion, MFMA wrappers and the activation functions used by epilogues.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tpcol {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 storage
+// bf16 values travel as raw uint16_t patterns.
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// float -> bf16 with round-to-nearest-even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  static constexpr int VW = 8;     // elements per 16-byte vector
+  static constexpr int KP = 8;     // k values per lane in one MFMA operand
+  static constexpr int KSTEP = 32; // k depth of one MFMA (16x16x32 bf16)
+  __device__ static float to_f(uint16_t v) { return bf2f(v); }
+  __device__ static uint16_t from_f(float v) { return f2bf(v); }
+};
+template <> struct Elem<float> {
+  static constexpr int VW = 4;
+  static constexpr int KP = 1;
+  static constexpr int KSTEP = 4;  // 16x16x4 fp32
+  __device__ static float to_f(float v) { return v; }
+  __device__ static float from_f(float v) { return v; }
+};
+
+// ---------------------------------------------------------------- MFMA
+// D[i][j] = sum_k A[i][k] B[k][j] + C for one 16x16 tile.  Lane l supplies
+// row (A) / column (B) l%16 and k-slots (l/16)*KP .. +KP-1; the result lane l
+// holds D[4*(l/16) + r][l%16], r = 0..3.
+__device__ __forceinline__ f32x4_t mfma16(const uint4 &a, const uint4 &b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t u4_word(const uint4 &v, int i) {
+  return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// ---------------------------------------------------------------- activations
+// Exact GELU z * Phi(z) = z/2 (1 + erf(z / sqrt 2)); erff is the device
+// library's single-precision error function.
+__device__ __forceinline__ float gelu_f(float z) {
+  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+}
+// d/dz GELU = Phi(z) + z phi(z)
+__device__ __forceinline__ float gelu_grad_f(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * 0.39894228040143268f * expf(-0.5f * z * z);
+}
+__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+__device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
+
+}  // namespace tpcol

@@ -1,0 +1,426 @@
+// Tiled MFMA GEMM for gfx950 with fused tensor-parallel epilogues.
+//
+//   C[M x N] = A[M x K] . B[K x N]   (fp32 accumulate)
+//
+// One kernel template serves every GEMM of the shard hot path:
+//   NN  column-parallel X.W_i (+GELU / SwiGLU / none), row-parallel partial
+//       X_i.W_i, QKV projection, and the backward recompute with the
+//       activation-derivative epilogue;
+//   NT  dgrad dY.W2_i^T and dZ.W1_i^T (the K-concatenated form covers
+//       dZg.Wg^T + dZu.Wu^T in one pass);
+//   TN  wgrad H^T.dY and X^T.dZ.
+//
+// Data path per workgroup (256 threads = 4 wave64):
+//   global --16-byte vector loads--> registers --> LDS tile [rows][BK+pad]
+//   (k contiguous; operands stored with the other dimension contiguous are
+//   transposed in registers on the way, 8x8 bf16 / 4x4 fp32 blocks) -->
+//   ds_read_b128 fragments --> v_mfma_f32_16x16x32_bf16 (fp32: 16x16x4f32).
+// The LDS tile is double-buffered: the next K-slab's global loads are in
+// flight while the current slab is multiplied, and one barrier per slab
+// separates reuse.  The MFMA is issued with B as the first operand so that
+// each lane ends up holding 4 consecutive output columns of one row, which
+// the epilogue writes as one vector.  The pre-activation never leaves
+// registers.
+//
+// Workgroup -> tile mapping is XCD-aware: the hardware deals consecutive
+// workgroup ids round-robin to the 8 XCDs, so ids are re-mapped so that each
+// XCD receives a contiguous run of tiles, which are then walked in groups of
+// GROUP_M tile-rows; neighbouring tiles share A rows / B columns in that
+// XCD's L2.
+#include <type_traits>
+
+#include "device_common.hpp"
+#include "kernels.hpp"
+
+namespace tpcol {
+
+struct GemmParams {
+  const void *A; int64_t lda;
+  const void *B; int64_t ldb;
+  const void *B2; int64_t ldb2;
+  const void *bias;
+  const void *D; int64_t ldd;
+  void *C; int64_t ldc;
+  void *C2; int64_t ldc2;
+  void *C3; int64_t ldc3;
+  int M, N, K, K1;
+  int tiles_m, tiles_n;
+};
+
+// rows x BK slab, k contiguous in global memory -> LDS [rows][LDK].
+template <typename T, int ROWS, int BK, int NT>
+struct DirectTile {
+  static constexpr int VW = Elem<T>::VW;
+  static constexpr int VPR = BK / VW;
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int PER = (NV + NT - 1) / NT;
+  uint4 r[PER];
+
+  template <bool KCAT>
+  __device__ __forceinline__ void load(const T *__restrict__ g, int64_t ld, const T *__restrict__ g2,
+                                       int64_t ld2, int K1, int row0, int rows_lim, int k0, int k_lim,
+                                       int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * NT;
+      r[i] = make_uint4(0u, 0u, 0u, 0u);
+      if ((NV % NT == 0) || v < NV) {
+        const int row = v / VPR, kv = v % VPR;
+        const int gr = row0 + row, gk = k0 + kv * VW;
+        if (gr < rows_lim && gk < k_lim) {
+          const T *src = (KCAT && gk >= K1) ? g2 + (int64_t)gr * ld2 + (gk - K1)
+                                            : g + (int64_t)gr * ld + gk;
+          r[i] = *reinterpret_cast<const uint4 *>(src);
+        }
+      }
+    }
+  }
+
+  template <int LDK>
+  __device__ __forceinline__ void store(T *s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int v = tid + i * NT;
+      if ((NV % NT == 0) || v < NV) {
+        const int row = v / VPR, kv = v % VPR;
+        *reinterpret_cast<uint4 *>(s + row * LDK + kv * VW) = r[i];
+      }
+    }
+  }
+};
+
+// BK x cols slab with cols contiguous in global memory -> LDS [cols][LDK]
+// (k contiguous): each thread moves VW x VW blocks and transposes them in
+// registers.
+template <typename T, int COLS, int BK, int NT>
+struct TransTile {
+  static constexpr int VW = Elem<T>::VW;
+  static constexpr int CB = COLS / VW;
+  static constexpr int KB = BK / VW;
+  static constexpr int NU = CB * KB;
+  static constexpr int PER = (NU + NT - 1) / NT;
+  uint4 r[PER][VW];
+
+  __device__ __forceinline__ void load(const T *__restrict__ g, int64_t ld, int col0, int col_lim,
+                                       int k0, int k_lim, int tid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      const bool valid = (NU % NT == 0) || u < NU;
+      const int cb = u % CB, kb = u / CB;
+      const int gc = col0 + cb * VW;
+#pragma unroll
+      for (int rr = 0; rr < VW; ++rr) {
+        const int gk = k0 + kb * VW + rr;
+        r[i][rr] = make_uint4(0u, 0u, 0u, 0u);
+        if (valid && gc < col_lim && gk < k_lim)
+          r[i][rr] = *reinterpret_cast<const uint4 *>(g + (int64_t)gk * ld + gc);
+      }
+    }
+  }
+
+  template <int LDK>
+  __device__ __forceinline__ void store(T *s, int tid) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int u = tid + i * NT;
+      if (!((NU % NT == 0) || u < NU)) continue;
+      const int cb = u % CB, kb = u / CB;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = u4_word(r[i][2 * q], c >> 1);
+            const uint32_t hi = u4_word(r[i][2 * q + 1], c >> 1);
+            w[q] = (c & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+          }
+          *reinterpret_cast<uint4 *>(s + (cb * 8 + c) * LDK + kb * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          *reinterpret_cast<uint4 *>(s + (cb * 4 + c) * LDK + kb * 4) =
+              make_uint4(u4_word(r[i][0], c), u4_word(r[i][1], c), u4_word(r[i][2], c),
+                         u4_word(r[i][3], c));
+        }
+      }
+    }
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ void load4(const T *p, float v[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 u = *reinterpret_cast<const uint2 *>(p);
+    v[0] = bf2f((uint16_t)(u.x & 0xffffu)); v[1] = bf2f((uint16_t)(u.x >> 16));
+    v[2] = bf2f((uint16_t)(u.y & 0xffffu)); v[3] = bf2f((uint16_t)(u.y >> 16));
+  } else {
+    const float4 f = *reinterpret_cast<const float4 *>(p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store4(T *p, const float v[4]) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int LAYOUT, int EPI, bool DUAL,
+          bool KCAT>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_kernel(GemmParams p) {
+  constexpr int NT = WGM * WGN * 64;
+  constexpr int VW = Elem<T>::VW, KP = Elem<T>::KP, KSTEP = Elem<T>::KSTEP;
+  constexpr int LDK = BK + VW;  // 16-byte row pad: conflict-free ds_read_b128 columns
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int STAGE = (BM + NB * BN) * LDK;
+  constexpr bool AT = (LAYOUT == LAY_TN);
+  constexpr bool BT = (LAYOUT == LAY_NT);
+  constexpr int GROUP_M = 4;
+  using Frag = typename std::conditional<sizeof(T) == 2, uint4, float>::type;
+  static_assert(BK % KSTEP == 0 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) T smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int M = p.M, N = p.N, K = p.K;
+
+  // ---- workgroup -> output tile (XCD-contiguous, then GROUP_M swizzle)
+  int tm, tn;
+  {
+    const int nblk = p.tiles_m * p.tiles_n;
+    const int b = blockIdx.x;
+    const int xcd = b & 7, idx = b >> 3, base = nblk >> 3, rem = nblk & 7;
+    const int lin = xcd * base + (xcd < rem ? xcd : rem) + idx;
+    const int per_group = GROUP_M * p.tiles_n;
+    const int group = lin / per_group;
+    const int first_m = group * GROUP_M;
+    const int gsz = min(p.tiles_m - first_m, GROUP_M);
+    const int in = lin - group * per_group;
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const T *__restrict__ Ag = static_cast<const T *>(p.A);
+  const T *__restrict__ Bg = static_cast<const T *>(p.B);
+  const T *__restrict__ B2g = static_cast<const T *>(p.B2);
+
+  typename std::conditional<AT, TransTile<T, BM, BK, NT>, DirectTile<T, BM, BK, NT>>::type la;
+  typename std::conditional<BT, DirectTile<T, BN, BK, NT>, TransTile<T, BN, BK, NT>>::type lb;
+  typename std::conditional<DUAL, TransTile<T, BN, BK, NT>, DirectTile<T, 16, BK, NT>>::type lb2;
+
+  auto load_slab = [&](int k0) {
+    if constexpr (AT) la.load(Ag, p.lda, m0, M, k0, K, tid);
+    else la.template load<false>(Ag, p.lda, nullptr, 0, 0, m0, M, k0, K, tid);
+    if constexpr (BT) lb.template load<KCAT>(Bg, p.ldb, B2g, p.ldb2, p.K1, n0, N, k0, K, tid);
+    else lb.load(Bg, p.ldb, n0, N, k0, K, tid);
+    if constexpr (DUAL) lb2.load(B2g, p.ldb2, n0, N, k0, K, tid);
+  };
+  auto store_slab = [&](int buf) {
+    T *As = smem + buf * STAGE;
+    la.template store<LDK>(As, tid);
+    lb.template store<LDK>(As + BM * LDK, tid);
+    if constexpr (DUAL) lb2.template store<LDK>(As + (BM + BN) * LDK, tid);
+  };
+
+  f32x4_t acc[TM][TN];
+  f32x4_t acc2[DUAL ? TM : 1][DUAL ? TN : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc2[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nk = (K + BK - 1) / BK;
+  load_slab(0);
+  store_slab(0);
+  __syncthreads();
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) load_slab((kt + 1) * BK);
+
+    const T *As = smem + cur * STAGE;
+    const T *Bs = As + BM * LDK;
+    const T *B2s = As + (BM + BN) * LDK;
+#pragma unroll
+    for (int kc = 0; kc < BK / KSTEP; ++kc) {
+      const int koff = kc * KSTEP + (lane >> 4) * KP;
+      Frag a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        a[i] = *reinterpret_cast<const Frag *>(As + (wm * WTM + i * 16 + (lane & 15)) * LDK + koff);
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        b[j] = *reinterpret_cast<const Frag *>(Bs + (wn * WTN + j * 16 + (lane & 15)) * LDK + koff);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(b[j], a[i], acc[i][j]);
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          b[j] = *reinterpret_cast<const Frag *>(B2s + (wn * WTN + j * 16 + (lane & 15)) * LDK + koff);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc2[i][j] = mfma16(b[j], a[i], acc2[i][j]);
+      }
+    }
+
+    if (kt + 1 < nk) store_slab(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds C[row][col .. col+3] of every 16x16 tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * WTM + i * 16 + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 16 + (lane >> 4) * 4;
+      if (row >= M || col >= N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      if (p.bias != nullptr) {
+        float bv[4];
+        if constexpr (EPI == EPI_STORE_F32) load4(static_cast<const float *>(p.bias) + col, bv);
+        else load4(static_cast<const T *>(p.bias) + col, bv);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] += bv[r];
+      }
+      const int64_t rowi = row;
+      if constexpr (EPI == EPI_STORE) {
+        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, v);
+      } else if constexpr (EPI == EPI_STORE_F32) {
+        store4(static_cast<float *>(p.C) + rowi * p.ldc + col, v);
+      } else if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
+        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, v);
+      } else if constexpr (EPI == EPI_SWIGLU) {
+        const float u[4] = {acc2[DUAL ? i : 0][DUAL ? j : 0][0], acc2[DUAL ? i : 0][DUAL ? j : 0][1],
+                            acc2[DUAL ? i : 0][DUAL ? j : 0][2], acc2[DUAL ? i : 0][DUAL ? j : 0][3]};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * u[r];
+        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, v);
+      } else if constexpr (EPI == EPI_GELU_BWD) {
+        float dh[4], dz[4], hh[4];
+        load4(static_cast<const T *>(p.D) + rowi * p.ldd + col, dh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dz[r] = dh[r] * gelu_grad_f(v[r]);
+          hh[r] = gelu_f(v[r]);
+        }
+        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, dz);
+        store4(static_cast<T *>(p.C2) + rowi * p.ldc2 + col, hh);
+      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
+        float dh[4], dzg[4], dzu[4], hh[4];
+        load4(static_cast<const T *>(p.D) + rowi * p.ldd + col, dh);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float g = v[r], u = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
+          const float sg = sigmoid_f(g);
+          const float sl = g * sg;
+          dzu[r] = dh[r] * sl;
+          dzg[r] = dh[r] * u * (sg * (1.0f + g * (1.0f - sg)));
+          hh[r] = sl * u;
+        }
+        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, dzg);
+        store4(static_cast<T *>(p.C3) + rowi * p.ldc3 + col, dzu);
+        store4(static_cast<T *>(p.C2) + rowi * p.ldc2 + col, hh);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+template <typename T, int BM, int BN, int BK, int WGM, int WGN, int LAYOUT, int EPI, bool DUAL,
+          bool KCAT>
+static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
+  GemmParams p;
+  p.A = a.A; p.lda = a.lda;
+  p.B = a.B; p.ldb = a.ldb;
+  p.B2 = a.B2; p.ldb2 = a.ldb2;
+  p.bias = a.bias;
+  p.D = a.D; p.ldd = a.ldd;
+  p.C = a.C; p.ldc = a.ldc;
+  p.C2 = a.C2; p.ldc2 = a.ldc2;
+  p.C3 = a.C3; p.ldc3 = a.ldc3;
+  p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K; p.K1 = (int)a.K1;
+  p.tiles_m = (int)((a.M + BM - 1) / BM);
+  p.tiles_n = (int)((a.N + BN - 1) / BN);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
+  hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WGM, WGN, LAYOUT, EPI, DUAL, KCAT>), grid,
+                     dim3(WGM * WGN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int LAYOUT, int EPI, bool DUAL, bool KCAT>
+static hipError_t pick_tile(const GemmArgs &a, hipStream_t s) {
+  if constexpr (sizeof(T) == 4) {
+    return run_gemm<T, 64, 64, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT>(a, s);
+  } else if constexpr (DUAL) {
+    const int64_t tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+    if (tiles >= 128) return run_gemm<T, 128, 128, 64, 2, 2, LAYOUT, EPI, DUAL, KCAT>(a, s);
+    return run_gemm<T, 64, 64, 64, 2, 2, LAYOUT, EPI, DUAL, KCAT>(a, s);
+  } else {
+    const int64_t tiles = ((a.M + 255) / 256) * ((a.N + 127) / 128);
+    if (tiles >= 128) return run_gemm<T, 256, 128, 64, 2, 2, LAYOUT, EPI, DUAL, KCAT>(a, s);
+    return run_gemm<T, 64, 64, 64, 2, 2, LAYOUT, EPI, DUAL, KCAT>(a, s);
+  }
+}
+
+template <typename T>
+static hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
+  switch (a.layout) {
+    case LAY_NN:
+      if (a.dual) {
+        if (a.epi == EPI_SWIGLU) return pick_tile<T, LAY_NN, EPI_SWIGLU, true, false>(a, s);
+        if (a.epi == EPI_SWIGLU_BWD) return pick_tile<T, LAY_NN, EPI_SWIGLU_BWD, true, false>(a, s);
+        return hipErrorInvalidValue;
+      }
+      switch (a.epi) {
+        case EPI_STORE: return pick_tile<T, LAY_NN, EPI_STORE, false, false>(a, s);
+        case EPI_STORE_F32: return pick_tile<T, LAY_NN, EPI_STORE_F32, false, false>(a, s);
+        case EPI_GELU: return pick_tile<T, LAY_NN, EPI_GELU, false, false>(a, s);
+        case EPI_GELU_BWD: return pick_tile<T, LAY_NN, EPI_GELU_BWD, false, false>(a, s);
+        default: return hipErrorInvalidValue;
+      }
+    case LAY_NT:
+      if (a.dual) return hipErrorInvalidValue;
+      if (a.kcat) {
+        if (a.epi == EPI_STORE_F32) return pick_tile<T, LAY_NT, EPI_STORE_F32, false, true>(a, s);
+        return hipErrorInvalidValue;
+      }
+      if (a.epi == EPI_STORE) return pick_tile<T, LAY_NT, EPI_STORE, false, false>(a, s);
+      if (a.epi == EPI_STORE_F32) return pick_tile<T, LAY_NT, EPI_STORE_F32, false, false>(a, s);
+      return hipErrorInvalidValue;
+    case LAY_TN:
+      if (a.dual || a.kcat || a.epi != EPI_STORE_F32) return hipErrorInvalidValue;
+      return pick_tile<T, LAY_TN, EPI_STORE_F32, false, false>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.dtype == DT_BF16) return dispatch<uint16_t>(a, s);
+  if (a.dtype == DT_F32) return dispatch<float>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace tpcol

@@ -1,0 +1,74 @@
+// Host-side interface between the C ABI (api.hip) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpcol {
+
+enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
+
+// Epilogue applied to the float32 accumulator(s) of a GEMM tile.
+enum Epi {
+  EPI_STORE = 0,      // C (dtype)   = acc + bias
+  EPI_STORE_F32 = 1,  // C (float32) = acc + bias
+  EPI_GELU = 2,       // C (dtype)   = GELU(acc + bias)
+  EPI_SWIGLU = 3,     // C (dtype)   = SiLU(acc) * acc2                  (dual)
+  EPI_GELU_BWD = 4,   // z = acc + bias, dh = D:  C = dh * GELU'(z), C2 = GELU(z)
+  EPI_SWIGLU_BWD = 5  // g = acc, u = acc2, dh = D: C = dh*u*SiLU'(g),
+                      //   C3 = dh*SiLU(g), C2 = SiLU(g)*u               (dual)
+};
+
+// Operand storage.  A is [M x K] row-major (N) or stored as its transpose
+// [K x M] row-major (T); B is [K x N] row-major (N) or stored as [N x K] (T).
+enum Layout { LAY_NN = 0, LAY_NT = 1, LAY_TN = 2 };
+
+struct GemmArgs {
+  int dtype = DT_BF16;
+  Layout layout = LAY_NN;
+  Epi epi = EPI_STORE;
+  bool dual = false;  // second B (B2) with its own accumulator (NN only)
+  bool kcat = false;  // B rows k >= K1 are read from B2 (NT only)
+  int64_t M = 0, N = 0, K = 0, K1 = 0;
+  const void *A = nullptr;  int64_t lda = 0;
+  const void *B = nullptr;  int64_t ldb = 0;
+  const void *B2 = nullptr; int64_t ldb2 = 0;
+  const void *bias = nullptr;                  // [N], dtype (f32 for EPI_STORE_F32)
+  const void *D = nullptr;  int64_t ldd = 0;   // epilogue input (dH), dtype
+  void *C = nullptr;  int64_t ldc = 0;
+  void *C2 = nullptr; int64_t ldc2 = 0;
+  void *C3 = nullptr; int64_t ldc3 = 0;
+};
+
+hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+
+// Decode GEMV (M <= 16): y = act(x W + bias) with split-K partials in ws.
+struct GemvArgs {
+  int dtype = DT_BF16;  // bf16 only
+  Epi epi = EPI_GELU;   // EPI_GELU / EPI_STORE (dtype out) or EPI_STORE_F32
+  int64_t M = 0, K = 0, N = 0;
+  const void *X = nullptr; int64_t ldx = 0;
+  const void *W = nullptr; int64_t ldw = 0;
+  const void *bias = nullptr;
+  void *Y = nullptr; int64_t ldy = 0;
+  void *ws = nullptr; size_t ws_bytes = 0;
+};
+size_t gemv_workspace(int64_t K, int64_t N);
+int64_t gemv_max_n();  // widest N the split-K decode path accepts
+hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
+
+// Y = sum_i P_i (+ bias), float32 partials, float32 or bf16 output.
+hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *parts,
+                            int64_t ldp, const float *bias, void *Y, int64_t ldy, hipStream_t s);
+
+// Head-local flash attention over a packed [Q|K|V] buffer (bf16, d = 128).
+hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, int64_t b,
+                             int64_t s, int64_t heads_local, int64_t d, bool causal,
+                             hipStream_t st);
+
+// db[n] = sum_m dZ[m][n] (dZ dtype, db float32).
+hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,
+                         hipStream_t s);
+
+}  // namespace tpcol

@@ -1,0 +1,146 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol that
+include/tpcol.h declares, and rejects bad arguments on the host before any
+launch.  No GPU compute is issued from here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import megatron_tensor_transformer_col_amd as tp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpcol.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tp.lib()
+    names = _declared()
+    assert len(names) >= 13
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tpcol.h but not exported"
+    assert set(names) == set(tp.EXPORTED_SYMBOLS)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        s = tp.tp_status_string(code)
+        assert s and s != "unknown status"
+    assert tp.tp_status_string(42) == "unknown status"
+
+
+@pytest.mark.parametrize("h,ffn,heads,n", [(128, 512, 8, 2), (4096, 14336, 32, 4), (1024, 4096, 16, 4),
+                                           (8192, 28672, 64, 8), (4096, 14336, 30, 4),
+                                           (4096, 14336, 32, 3), (100, 512, 8, 2), (128, 513, 8, 2),
+                                           (128, 512, 0, 2), (128, 512, 8, 0)])
+def test_check_split_matches_divisibility(h, ffn, heads, n):
+    ok = n >= 1 and ffn % n == 0 and (heads == 0 or (h % heads == 0 and heads % n == 0))
+    assert (tp.tp_check_split(h, ffn, heads, n) == 0) == ok
+
+
+def test_gemv_threshold_option():
+    prev = tp.tp_set_gemv_max_m(8)
+    try:
+        assert tp.tp_set_gemv_max_m(16) == 8
+        with pytest.raises(tp.TpError):
+            tp.tp_set_gemv_max_m(17)
+        with pytest.raises(tp.TpError):
+            tp.tp_set_gemv_max_m(-1)
+    finally:
+        tp.tp_set_gemv_max_m(prev)
+
+
+def test_workspace_sizes():
+    # attention: QKV [T x 3 hl d] + O [T x hl d] bf16, 256-byte aligned regions
+    T = 4 * 2048
+    assert tp.tp_attn_heads_shard_workspace(1, 4, 2048, 8, 128) == T * 3 * 1024 * 2 + T * 1024 * 2
+    # backward: dH, H, dZ (GELU) / dH, H, [dZg | dZu] (SwiGLU)
+    assert tp.tp_mlp_shard_backward_workspace(1, 1, 8192, 1024) == 3 * 8192 * 1024 * 2
+    assert tp.tp_mlp_shard_backward_workspace(1, 2, 8192, 3584) == 4 * 8192 * 3584 * 2
+    assert tp.tp_mlp_shard_backward_workspace(0, 1, 32, 256) == 3 * 32 * 256 * 4
+    # large-M linear calls need no workspace; the decode path needs split-K partials
+    assert tp.tp_col_linear_gelu_workspace(1, 1, 8192, 1024, 1024) == 0
+    assert tp.tp_col_linear_gelu_workspace(1, 1, 16, 8192, 3584) > 0
+    assert tp.tp_col_linear_gelu_workspace(0, 1, 16, 8192, 3584) == 0   # fp32 has no GEMV path
+    assert tp.tp_row_linear_partial_workspace(1, 16, 3584, 8192) > 0
+
+
+# ---------------------------------------------------------------- host validation
+# Fake device addresses are never dereferenced: each case must be rejected by
+# the host-side checks.  Skipped where a GPU is visible so that a validation
+# bug can never turn into a launch on bogus pointers.
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+host_only = pytest.mark.skipif(_gpu_visible(), reason="fake-pointer validation runs on CPU hosts only")
+
+A = 1 << 20          # 16-byte aligned fake address
+MIS = A + 2          # misaligned
+V = ctypes.c_void_p
+
+
+@host_only
+@pytest.mark.parametrize("case,expect", [
+    ("bad_dtype", -4), ("bad_act", -1), ("null_x", -1), ("misaligned_w", -3), ("ld_small", -2),
+    ("odd_width", -3), ("swiglu_no_up", -1), ("swiglu_bias", -1), ("gemv_no_ws", -5),
+    ("neg_m", -2),
+])
+def test_col_linear_validation(case, expect):
+    lib = tp.lib()
+    a = dict(dt=1, act=1, M=64, K=256, N=512, X=A, ldx=256, W=A, ldw=512, Wu=None, ldwu=0,
+             bias=None, H=A, ldh=512, ws=None, nws=0)
+    if case == "bad_dtype": a["dt"] = 7
+    if case == "bad_act": a["act"] = 9
+    if case == "null_x": a["X"] = None
+    if case == "misaligned_w": a["W"] = MIS
+    if case == "ld_small": a["ldh"] = 256
+    if case == "odd_width": a.update(N=500, ldw=504, ldh=504)
+    if case == "swiglu_no_up": a["act"] = 2
+    if case == "swiglu_bias": a.update(act=2, Wu=A, ldwu=512, bias=A)
+    if case == "gemv_no_ws": a.update(M=4, K=4096, ldx=4096)
+    if case == "neg_m": a["M"] = -1
+    st = lib.tp_col_linear_gelu(a["dt"], a["act"], a["M"], a["K"], a["N"], a["X"], a["ldx"], a["W"],
+                                a["ldw"], a["Wu"], a["ldwu"], a["bias"], a["H"], a["ldh"], a["ws"],
+                                a["nws"], None)
+    assert st == expect, tp.tp_last_error()
+    assert tp.tp_last_error()
+
+
+@host_only
+def test_attention_validation():
+    lib = tp.lib()
+    f = lib.tp_attn_heads_shard
+    # fp32 is not supported
+    assert f(0, 4, 2048, 4096, 8, 128, 1, A, 4096, A, 3072, A, 4096, A, 4096, A, 1 << 30, None) == -4
+    # head dim other than 128
+    assert f(1, 4, 2048, 4096, 8, 64, 1, A, 4096, A, 1536, A, 4096, A, 4096, A, 1 << 30, None) == -2
+    # workspace too small
+    assert f(1, 4, 2048, 4096, 8, 128, 1, A, 4096, A, 3072, A, 4096, A, 4096, A, 1024, None) == -5
+    # Wqkv narrower than 3 * heads_local * d
+    assert f(1, 4, 2048, 4096, 8, 128, 1, A, 4096, A, 2048, A, 4096, A, 4096, A, 1 << 30, None) == -2
+
+
+@host_only
+def test_shard_sum_and_backward_validation():
+    lib = tp.lib()
+    arr = (V * 3)(A, A, None)
+    assert lib.tp_shard_sum(0, 16, 64, 3, arr, 64, None, A, 64, None) == -1     # NULL partial
+    assert lib.tp_shard_sum(0, 16, 64, 0, arr, 64, None, A, 64, None) == -1     # n = 0
+    assert lib.tp_shard_sum(0, 16, 64, 65, arr, 64, None, A, 64, None) == -1    # n > 64
+    assert lib.tp_shard_sum(1, 16, 68, 2, arr, 68, None, A, 68, None) == -3     # bf16 width 68
+    bw = lib.tp_mlp_shard_backward
+    common = (A, 256, A, 128, None, 0, None, A, 256, A, 256, A, None, A, None, A, 256)
+    assert bw(1, 0, 64, 256, 128, *common, A, 1 << 30, None) == -1               # act NONE
+    assert bw(1, 1, 64, 256, 128, *common, A, 100, None) == -5                   # tiny workspace
+    assert bw(1, 2, 64, 256, 128, *common, A, 1 << 30, None) == -1               # SwiGLU w/o Wup

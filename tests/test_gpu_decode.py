@@ -1,0 +1,83 @@
+"""GPU parity of the decode (M <= 16) weight-streaming GEMV path."""
+import numpy as np
+import pytest
+
+import megatron_tensor_transformer_col_amd as tp
+import oracle
+import synth
+from gpu_util import assert_close, dev, empty, host, note, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_mlp_full_size():
+    """16 tokens, h=8192, ffn=28672, N=8: all 8 shards + shard sum."""
+    W = synth.WORKLOADS["decode_mlp_bf16"]
+    note("decode MLP full size")
+    d = synth.make_mlp_inputs(W.tokens, W.h, W.ffn, "bf16", seed=W.seed, row_block=1024)
+    X = dev(d["X"])
+    n, w = W.n_shards, W.ffn_shard
+    ref = oracle.mlp_gelu(d["X"].f32, d["W1"].f32, d["W2"].f32)
+    Ps = []
+    for i in range(n):
+        H = empty((W.tokens, w), "bf16")
+        tp.tp_col_linear_gelu(X, dev(synth.column_shard(d["W1"], i, n)), H)
+        P = empty((W.tokens, W.h), "f32")
+        tp.tp_row_linear_partial(H, dev(synth.row_shard(d["W2"], i, n)), P)
+        torch().cuda.synchronize()
+        assert_close(host(H), ref["H"][:, i * w:(i + 1) * w], "bf16", f"H_{i}")
+        Ps.append(P)
+    Y = empty((W.tokens, W.h), "f32")
+    tp.tp_shard_sum(Ps, Y)
+    torch().cuda.synchronize()
+    assert_close(host(Y), ref["Y"], "bf16", "Y")
+
+
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+@pytest.mark.parametrize("K,N", [(64, 136), (1024, 520), (4104, 1032)])
+def test_gemv_integer_exact(M, K, N):
+    note(f"gemv exact M={M} K={K} N={N}")
+    rng = np.random.default_rng(M * 131 + K)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    Wm = rng.integers(-2, 3, size=(K, N)).astype(np.float32)
+    P = empty((M, N), "f32", fill=float("nan"))
+    tp.tp_row_linear_partial(dev(synth.Tensor(X, "bf16", synth.round_to_bf16_bits(X))),
+                             dev(synth.Tensor(Wm, "bf16", synth.round_to_bf16_bits(Wm))), P)
+    torch().cuda.synchronize()
+    assert np.array_equal(host(P), (X.astype(np.int64) @ Wm.astype(np.int64)).astype(np.float64))
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_gemv_matches_gemm_path_and_oracle(M):
+    note(f"gemv vs gemm M={M}")
+    d = synth.make_mlp_inputs(M, 2048, 1536, "bf16", seed=M, with_bias=True)
+    X, W1 = dev(d["X"]), dev(d["W1"])
+    b1 = dev(d["b1"])[0]
+    Hv = empty((M, 1536), "bf16")
+    tp.tp_col_linear_gelu(X, W1, Hv, bias=b1)
+    prev = tp.tp_set_gemv_max_m(0)
+    try:
+        Hm = empty((M, 1536), "bf16")
+        tp.tp_col_linear_gelu(X, W1, Hm, bias=b1)
+    finally:
+        tp.tp_set_gemv_max_m(prev)
+    torch().cuda.synchronize()
+    ref = oracle.gelu(oracle.linear(d["X"].f32, d["W1"].f32, d["b1"].f32[0]))
+    assert_close(host(Hv), ref, "bf16", "H gemv")
+    assert_close(host(Hm), ref, "bf16", "H gemm")
+
+
+def test_gemv_repeated_calls_reset_counters():
+    # the split-K arrival counters must be left at zero for the next call
+    note("gemv repeated")
+    rng = np.random.default_rng(0)
+    X = rng.integers(-2, 3, size=(16, 2048)).astype(np.float32)
+    Wm = rng.integers(-2, 3, size=(2048, 1024)).astype(np.float32)
+    Xd = dev(synth.Tensor(X, "bf16", synth.round_to_bf16_bits(X)))
+    Wd = dev(synth.Tensor(Wm, "bf16", synth.round_to_bf16_bits(Wm)))
+    exact = (X.astype(np.int64) @ Wm.astype(np.int64)).astype(np.float64)
+    for it in range(5):
+        P = empty((16, 1024), "f32", fill=float("nan"))
+        tp.tp_row_linear_partial(Xd, Wd, P)
+        torch().cuda.synchronize()
+        assert np.array_equal(host(P), exact), it
