@@ -1,6 +1,7 @@
 """Benchmark of the tensor-parallel shard hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-rows] [--no-cpu]
+    python bench.py --op NAME [--iters N]      # one kernel family, for rocprofv3
 
 Headline workload (one "step"): the GPT-2-medium-shaped TP MLP layer,
 tokens b*s = 8*1024, h = 1024, ffn = 4096 split into N = 4 shards, all four
@@ -40,6 +41,8 @@ def parse():
     ap.add_argument("--no-rows", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--op", default=None, help="run one op repeatedly (profiling)")
+    ap.add_argument("--iters", type=int, default=100)
     return ap.parse_args()
 
 
@@ -90,135 +93,230 @@ def timed(torch, step, steps, warmup):
 
 
 # --------------------------------------------------------------------------- headline
-def headline(torch, tp, synth, steps, warmup):
-    W = synth.WORKLOADS["gpt2m_mlp_bf16"]
-    d = synth.make_mlp_inputs(W.tokens, W.h, W.ffn, "bf16", seed=W.seed)
-    n, T, h, f = W.n_shards, W.tokens, W.h, W.ffn_shard
-    X = dev(d["X"], torch)
-    W1 = [dev(synth.column_shard(d["W1"], i, n), torch) for i in range(n)]
-    W2 = [dev(synth.row_shard(d["W2"], i, n), torch) for i in range(n)]
-    H = [torch.empty((T, f), dtype=torch.bfloat16, device="cuda:0") for _ in range(n)]
-    P = [torch.empty((T, h), dtype=torch.float32, device="cuda:0") for _ in range(n)]
-    Y = torch.empty((T, h), dtype=torch.float32, device="cuda:0")
+class Headline:
+    """gpt2m_mlp_bf16 inputs (numpy PCG64 seed 0, the same draws as the parity tests)."""
 
-    def step(kt):
-        for i in range(n):
+    def __init__(self, torch, tp, synth):
+        W = synth.WORKLOADS["gpt2m_mlp_bf16"]
+        d = synth.make_mlp_inputs(W.tokens, W.h, W.ffn, "bf16", seed=W.seed)
+        self.W = W
+        n, T, h, f = W.n_shards, W.tokens, W.h, W.ffn_shard
+        self.n, self.T, self.h, self.f = n, T, h, f
+        self.X = dev(d["X"], torch)
+        self.W1 = [dev(synth.column_shard(d["W1"], i, n), torch) for i in range(n)]
+        self.W2 = [dev(synth.row_shard(d["W2"], i, n), torch) for i in range(n)]
+        self.H = [torch.empty((T, f), dtype=torch.bfloat16, device="cuda:0") for _ in range(n)]
+        self.P = [torch.empty((T, h), dtype=torch.float32, device="cuda:0") for _ in range(n)]
+        self.Y = torch.empty((T, h), dtype=torch.float32, device="cuda:0")
+        self.tp = tp
+        self.gemm_flops = 2.0 * T * h * f
+
+    def col(self, i):
+        self.tp.tp_col_linear_gelu(self.X, self.W1[i], self.H[i])
+
+    def row(self, i):
+        self.tp.tp_row_linear_partial(self.H[i], self.W2[i], self.P[i])
+
+    def total(self):
+        self.tp.tp_shard_sum(self.P, self.Y)
+
+    def step(self, kt):
+        for i in range(self.n):
             if kt is None:
-                tp.tp_col_linear_gelu(X, W1[i], H[i])
+                self.col(i)
             else:
-                kt.region(lambda i=i: tp.tp_col_linear_gelu(X, W1[i], H[i]))
-            tp.tp_row_linear_partial(H[i], W2[i], P[i])
-        tp.tp_shard_sum(P, Y)
+                kt.region(lambda i=i: self.col(i))
+            self.row(i)
+        self.total()
 
-    ms, kt = timed(torch, step, steps, warmup)
-    gemm_flops = 2.0 * T * h * f
-    step_flops = 2 * n * gemm_flops
+
+def headline(torch, tp, synth, steps, warmup):
+    hl = Headline(torch, tp, synth)
+    ms, kt = timed(torch, hl.step, steps, warmup)
+    step_flops = 2 * hl.n * hl.gemm_flops
     col_ms = kt.mean_ms()
-    col_tflops = gemm_flops / (col_ms * 1e-3) / 1e12
     return {
         "ms": ms, "tflops": step_flops / (ms * 1e-3) / 1e12, "step_flops": step_flops,
-        "col_ms": col_ms, "col_tflops": col_tflops, "gemm_flops": gemm_flops,
+        "col_ms": col_ms, "col_tflops": hl.gemm_flops / (col_ms * 1e-3) / 1e12,
+        "gemm_flops": hl.gemm_flops,
         "config": {"workload": "gpt2m_mlp_bf16: TP MLP layer, tokens 8x1024, h 1024, ffn 4096, "
                                "4 shards in sequence + shard sum",
-                   "tokens": T, "h": h, "ffn": W.ffn, "n_shards": n, "activation": "gelu_erf"},
+                   "tokens": hl.T, "h": hl.h, "ffn": hl.W.ffn, "n_shards": hl.n,
+                   "activation": "gelu_erf"},
     }
 
 
-# --------------------------------------------------------------------------- other rows
-def rows(torch, tp, steps, warmup):
-    g = torch.Generator(device="cuda:0")
-    g.manual_seed(0)
+# --------------------------------------------------------------------------- other workloads
+class Rows:
+    """The other workloads, at their full per-shard sizes.  Inputs come from a
+    seeded device generator (torch.Generator on cuda:0, seed 0) with the same
+    distributions as the parity tests: activations N(0,1), weights N(0,0.02^2),
+    rounded to bf16."""
 
-    def randn(shape, std):
-        return (torch.randn(shape, generator=g, device="cuda:0", dtype=torch.float32) * std).to(torch.bfloat16)
+    def __init__(self, torch, tp):
+        self.torch, self.tp = torch, tp
+        self.g = torch.Generator(device="cuda:0")
+        self.g.manual_seed(0)
 
-    out = {}
+    def randn(self, shape, std):
+        t = self.torch
+        return (t.randn(shape, generator=self.g, device="cuda:0", dtype=t.float32) * std).to(t.bfloat16)
+
+    def empty(self, shape, dtype):
+        return self.torch.empty(shape, dtype=dtype, device="cuda:0")
+
     # ---- Llama-style SwiGLU shard: T 8192, h 4096, ffn 14336 / 4
-    T, h, f = 8192, 4096, 3584
-    X, dY = randn((T, h), 1.0), randn((T, h), 1.0)
-    Wg, Wu, Wd = randn((h, f), 0.02), randn((h, f), 0.02), randn((f, h), 0.02)
-    H = torch.empty((T, f), dtype=torch.bfloat16, device="cuda:0")
-    P = torch.empty((T, h), dtype=torch.float32, device="cuda:0")
-    dWg = torch.empty((h, f), dtype=torch.float32, device="cuda:0")
-    dWu = torch.empty_like(dWg)
-    dWd = torch.empty((f, h), dtype=torch.float32, device="cuda:0")
-    dXi = torch.empty((T, h), dtype=torch.float32, device="cuda:0")
+    def swiglu(self):
+        t = self.torch
+        T, h, f = 8192, 4096, 3584
+        s = {"X": self.randn((T, h), 1.0), "dY": self.randn((T, h), 1.0),
+             "Wg": self.randn((h, f), 0.02), "Wu": self.randn((h, f), 0.02),
+             "Wd": self.randn((f, h), 0.02)}
+        s["H"] = self.empty((T, f), t.bfloat16)
+        s["P"] = self.empty((T, h), t.float32)
+        s["dWg"] = self.empty((h, f), t.float32)
+        s["dWu"] = self.empty((h, f), t.float32)
+        s["dWd"] = self.empty((f, h), t.float32)
+        s["dXi"] = self.empty((T, h), t.float32)
+        s["flop_gemm"] = 2.0 * T * h * f
+        return s
 
-    def fwd(kt):
-        tp.tp_col_linear_gelu(X, Wg, H, act="swiglu", Wup=Wu)
-        tp.tp_row_linear_partial(H, Wd, P)
+    def swiglu_col(self, s):
+        self.tp.tp_col_linear_gelu(s["X"], s["Wg"], s["H"], act="swiglu", Wup=s["Wu"])
 
-    def bwd(kt):
-        tp.tp_mlp_shard_backward(X, Wg, Wd, dY, dWg, dWd, dXi, act="swiglu", Wup=Wu, dWup=dWu)
+    def swiglu_down(self, s):
+        self.tp.tp_row_linear_partial(s["H"], s["Wd"], s["P"])
 
+    def swiglu_bwd(self, s):
+        self.tp.tp_mlp_shard_backward(s["X"], s["Wg"], s["Wd"], s["dY"], s["dWg"], s["dWd"], s["dXi"],
+                                      act="swiglu", Wup=s["Wu"], dWup=s["dWu"])
+
+    # ---- head-sharded MHA: b 4, s 2048, h 4096, 8 local heads of 128
+    def mha(self):
+        t = self.torch
+        b, sq, h, hl, dh = 4, 2048, 4096, 8, 128
+        T = b * sq
+        s = {"X": self.randn((T, h), 1.0), "Wqkv": self.randn((h, 3 * hl * dh), 0.02),
+             "Wo": self.randn((hl * dh, h), 0.02), "P": self.empty((T, h), t.float32),
+             "dims": (b, sq, hl, dh)}
+        s["ws"] = self.empty((self.tp.tp_attn_heads_shard_workspace(1, b, sq, hl, dh),), t.uint8)
+        s["flop_qkv"] = 2.0 * T * h * 3 * hl * dh
+        s["flop_att"] = 4.0 * dh * (sq * (sq + 1) / 2) * b * hl
+        s["flop_o"] = 2.0 * T * hl * dh * h
+        return s
+
+    def attn(self, s):
+        b, sq, hl, dh = s["dims"]
+        self.tp.tp_attn_heads_shard(s["X"], s["Wqkv"], s["Wo"], s["P"], b, sq, hl, dh, causal=True,
+                                    ws=s["ws"])
+
+    # ---- decode GEMV: 16 tokens, h 8192, ffn 28672 / 8, all 8 shards
+    #      (940 MB of weights > the 256 MB Infinity Cache: every GEMV streams from HBM)
+    def decode(self):
+        t = self.torch
+        M, h, f, n = 16, 8192, 3584, 8
+        s = {"x": self.randn((M, h), 1.0), "n": n, "M": M, "h": h, "f": f}
+        s["W1"] = [self.randn((h, f), 0.02) for _ in range(n)]
+        s["W2"] = [self.randn((f, h), 0.02) for _ in range(n)]
+        s["H"] = [self.empty((M, f), t.bfloat16) for _ in range(n)]
+        s["P"] = [self.empty((M, h), t.float32) for _ in range(n)]
+        s["Y"] = self.empty((M, h), t.float32)
+        s["w_bytes"] = 2.0 * h * f
+        return s
+
+    def decode_step(self, s):
+        for i in range(s["n"]):
+            self.tp.tp_col_linear_gelu(s["x"], s["W1"][i], s["H"][i])
+            self.tp.tp_row_linear_partial(s["H"][i], s["W2"][i], s["P"][i])
+        self.tp.tp_shard_sum(s["P"], s["Y"])
+
+
+def rows(torch, tp, steps, warmup):
+    R = Rows(torch, tp)
+    out = {}
     s_ms = min(steps, 20)
-    ms_f, _ = timed(torch, fwd, s_ms, min(warmup, 3))
-    ms_b, _ = timed(torch, bwd, s_ms, min(warmup, 3))
-    flop_f = 2.0 * T * h * f * 3
-    flop_b = 2.0 * T * h * f * 6            # algorithmic: dgrad x3 + wgrad x3
+    w_ms = min(warmup, 3)
+    s = R.swiglu()
+    ms_f, _ = timed(torch, lambda kt: (R.swiglu_col(s), R.swiglu_down(s)), s_ms, w_ms)
+    ms_b, _ = timed(torch, lambda kt: R.swiglu_bwd(s), s_ms, w_ms)
+    flop_f, flop_b = 3 * s["flop_gemm"], 6 * s["flop_gemm"]
     out["llama_swiglu_fwd"] = {"ms": ms_f, "tflops": flop_f / ms_f / 1e9,
                                "frac_peak": flop_f / ms_f / 1e9 / PEAK_BF16_TFLOPS}
     out["llama_swiglu_bwd"] = {"ms": ms_b, "tflops": flop_b / ms_b / 1e9,
                                "frac_peak": flop_b / ms_b / 1e9 / PEAK_BF16_TFLOPS,
-                               "note": "algorithmic flops; the Z recompute (+2*T*h*f*2) is not counted"}
-    del X, dY, Wg, Wu, Wd, H, P, dWg, dWu, dWd, dXi
-
-    # ---- head-sharded MHA: b 4, s 2048, h 4096, 8 local heads of 128
-    b, s, h, hl, dh = 4, 2048, 4096, 8, 128
-    T = b * s
-    X = randn((T, h), 1.0)
-    Wqkv, Wo = randn((h, 3 * hl * dh), 0.02), randn((hl * dh, h), 0.02)
-    P = torch.empty((T, h), dtype=torch.float32, device="cuda:0")
-    ws = torch.empty(tp.tp_attn_heads_shard_workspace(1, b, s, hl, dh), dtype=torch.uint8, device="cuda:0")
-
-    def attn(kt):
-        tp.tp_attn_heads_shard(X, Wqkv, Wo, P, b, s, hl, dh, causal=True, ws=ws)
-
-    ms_a, _ = timed(torch, attn, s_ms, min(warmup, 3))
-    flop_qkv = 2.0 * T * h * 3 * hl * dh
-    flop_att = 4.0 * dh * (s * (s + 1) / 2) * b * hl
-    flop_o = 2.0 * T * hl * dh * h
-    fa = flop_qkv + flop_att + flop_o
+                               "note": "algorithmic flops (dgrad x3 + wgrad x3); the Z recompute "
+                                       "(+2 GEMMs) is not counted"}
+    del s
+    s = R.mha()
+    ms_a, _ = timed(torch, lambda kt: R.attn(s), s_ms, w_ms)
+    fa = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
     out["mha_heads_shard"] = {"ms": ms_a, "tflops": fa / ms_a / 1e9,
                               "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
-                              "note": "causal attention counted as 4*d*s(s+1)/2 per head"}
-    del X, Wqkv, Wo, P, ws
-
-    # ---- decode GEMV: 16 tokens, h 8192, ffn 28672 / 8; all 8 shards per step
-    #      (940 MB of weights > the 256 MB Infinity Cache, so each GEMV streams from HBM)
-    M, h, f, n = 16, 8192, 3584, 8
-    x = randn((M, h), 1.0)
-    W1 = [randn((h, f), 0.02) for _ in range(n)]
-    W2 = [randn((f, h), 0.02) for _ in range(n)]
-    Hd = [torch.empty((M, f), dtype=torch.bfloat16, device="cuda:0") for _ in range(n)]
-    Pd = [torch.empty((M, h), dtype=torch.float32, device="cuda:0") for _ in range(n)]
-    Yd = torch.empty((M, h), dtype=torch.float32, device="cuda:0")
-
-    def dec(kt):
-        for i in range(n):
-            tp.tp_col_linear_gelu(x, W1[i], Hd[i])
-            tp.tp_row_linear_partial(Hd[i], W2[i], Pd[i])
-        tp.tp_shard_sum(Pd, Yd)
-
-    # capture the 17 launches in a graph so the GPU never waits on the host
+                              "note": "QKV GEMM + causal attention (4*d*s(s+1)/2 per head) + W_o GEMM"}
+    del s
+    s = R.decode()
     for _ in range(3):
-        dec(None)
+        R.decode_step(s)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
-        dec(None)
+        R.decode_step(s)
     ms_d, _ = timed(torch, lambda kt: graph.replay(), s_ms, 3)
-    w_bytes = n * 2 * (2.0 * h * f)
+    w_bytes = s["n"] * 2 * s["w_bytes"]
     out["decode_gemv"] = {"ms_step": ms_d, "weight_bytes": w_bytes,
                           "gbs": w_bytes / ms_d / 1e6, "frac_hbm_peak": w_bytes / ms_d / 1e6 / PEAK_HBM_GBS,
-                          "note": "weights of 16 GEMVs (8 shards x 2) + shard sum per graph replay; "
+                          "note": "16 GEMVs (8 shards x col + row) + shard sum per HIP-graph replay; "
                                   "GB/s counts weight bytes only"}
     return out
 
 
+# --------------------------------------------------------------------------- single ops
+def run_op(torch, tp, synth, name, iters):
+    """Run one op `iters` times after a warm-up and print its mean time."""
+    if name.startswith("c2_"):
+        hl = Headline(torch, tp, synth)
+        fn = {"c2_col": lambda: hl.col(0), "c2_row": lambda: hl.row(0), "c2_sum": hl.total,
+              "c2_step": lambda: hl.step(None)}[name]
+    else:
+        R = Rows(torch, tp)
+        if name.startswith("c3_"):
+            s = R.swiglu()
+            fn = {"c3_col": lambda: R.swiglu_col(s), "c3_down": lambda: R.swiglu_down(s),
+                  "c3_bwd": lambda: R.swiglu_bwd(s)}[name]
+        elif name == "c4_attn":
+            s = R.mha()
+            fn = lambda: R.attn(s)
+        elif name.startswith("c5_"):
+            s = R.decode()
+            k = {"c5_col": 0, "c5_row": 1}[name]
+            it = [0]
+
+            def fn():
+                i = it[0] % s["n"]
+                it[0] += 1
+                if k == 0:
+                    tp.tp_col_linear_gelu(s["x"], s["W1"][i], s["H"][i])
+                else:
+                    tp.tp_row_linear_partial(s["H"][i], s["W2"][i], s["P"][i])
+        else:
+            raise SystemExit(f"unknown op {name}")
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"op": name, "iters": iters, "ms_per_iter": a.elapsed_time(b) / iters,
+                      "wall_s": time.perf_counter() - t0}), flush=True)
+
+
 # --------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(synth, seconds):
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -258,6 +356,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.op:
+        run_op(torch, tp, synth, args.op, args.iters)
+        return
 
     hl = headline(torch, tp, synth, args.steps, args.warmup)
     result = {
@@ -265,7 +366,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(hl["ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": hl["config"],
-        "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU (gemm_kernel NN, EPI_GELU)",
+        "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU epilogue (gemm_lds_kernel NN)",
                      "achieved": round(hl["col_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(hl["col_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "avg_launch_us": round(hl["col_ms"] * 1e3, 3),

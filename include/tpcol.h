@@ -80,10 +80,8 @@ typedef enum {
  *   H    [M x Ni]  ldh         dtype   (output)
  * M <= the GEMV threshold (16 by default) selects the weight-streaming decode
  * path, which needs tp_col_linear_gelu_workspace() bytes of ws (256-byte
- * aligned) when K > 512.  Its first 64 KiB hold split-K arrival counters:
- * they must be zero before the first use of the buffer, every completed call
- * leaves them zero again, and buffers may be shared by calls of any shape
- * (not concurrently).  Larger M needs no workspace (ws may be NULL).
+ * aligned scratch for split-K partial sums; contents on entry do not
+ * matter).  Larger M needs no workspace (ws may be NULL).
  */
 int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni,
                        const void *X, int64_t ldx,

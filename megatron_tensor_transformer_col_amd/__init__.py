@@ -141,9 +141,8 @@ def _stream(stream, ref):
 
 
 class _WorkspaceCache:
-    """Per-device scratch buffers owned by the binding.  ``zeroed`` buffers
-    are only used by calls that leave them zeroed again (the decode GEMV's
-    arrival counters); the other pool is plain scratch."""
+    """Per-device scratch buffers owned by the binding, one pool for the
+    linear calls' decode path and one for attention / backward."""
 
     def __init__(self):
         self._bufs = {}

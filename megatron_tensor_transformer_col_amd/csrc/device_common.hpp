@@ -59,17 +59,45 @@ __device__ __forceinline__ uint32_t u4_word(const uint4 &v, int i) {
 }
 
 // ---------------------------------------------------------------- activations
-// Exact GELU z * Phi(z) = z/2 (1 + erf(z / sqrt 2)); erff is the device
-// library's single-precision error function.
-__device__ __forceinline__ float gelu_f(float z) {
-  return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f));
+// Standard normal CDF Phi(z) = (1 + erf(z / sqrt 2)) / 2 without branches,
+// from the erf approximation of Abramowitz & Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26 (|error of erf| <= 1.5e-7):
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x),  x >= 0.
+// For z < 0 the tail is taken directly (Phi(z) = q / 2), so there is no
+// cancellation for large negative z.  exp(-x^2) comes back as well, for the
+// density term of GELU'.
+struct PhiResult {
+  float phi_cdf;  // Phi(z)
+  float pdf;      // standard normal density exp(-z^2 / 2) / sqrt(2 pi)
+};
+__device__ __forceinline__ PhiResult normal_cdf_pdf(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;  // |z| / sqrt 2
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-x * x * 1.4426950408889634f);  // exp(-x^2)
+  const float q = poly * e;                                               // erfc(x)
+  PhiResult r;
+  r.phi_cdf = z >= 0.0f ? fmaf(-0.5f, q, 1.0f) : 0.5f * q;
+  r.pdf = 0.39894228040143268f * e;
+  return r;
 }
+
+// Exact-form GELU z * Phi(z) ("张量并行", MLP 层的并行化).
+__device__ __forceinline__ float gelu_f(float z) { return z * normal_cdf_pdf(z).phi_cdf; }
 // d/dz GELU = Phi(z) + z phi(z)
 __device__ __forceinline__ float gelu_grad_f(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
-         z * 0.39894228040143268f * expf(-0.5f * z * z);
+  const PhiResult r = normal_cdf_pdf(z);
+  return fmaf(z, r.pdf, r.phi_cdf);
 }
-__device__ __forceinline__ float sigmoid_f(float z) { return 1.0f / (1.0f + expf(-z)); }
+// sigmoid(z) = 1 / (1 + exp(-z)) with the hardware exp2 / reciprocal
+__device__ __forceinline__ float sigmoid_f(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z * 1.4426950408889634f));
+}
 __device__ __forceinline__ float silu_f(float z) { return z * sigmoid_f(z); }
 
 }  // namespace tpcol

@@ -29,23 +29,9 @@
 // XCD's L2.
 #include <type_traits>
 
-#include "device_common.hpp"
-#include "kernels.hpp"
+#include "gemm_common.hpp"
 
 namespace tpcol {
-
-struct GemmParams {
-  const void *A; int64_t lda;
-  const void *B; int64_t ldb;
-  const void *B2; int64_t ldb2;
-  const void *bias;
-  const void *D; int64_t ldd;
-  void *C; int64_t ldc;
-  void *C2; int64_t ldc2;
-  void *C3; int64_t ldc3;
-  int M, N, K, K1;
-  int tiles_m, tiles_n;
-};
 
 // rows x BK slab, k contiguous in global memory -> LDS [rows][LDK].
 template <typename T, int ROWS, int BK, int NT>
@@ -150,27 +136,6 @@ struct TransTile {
   }
 };
 
-template <typename T>
-__device__ __forceinline__ void load4(const T *p, float v[4]) {
-  if constexpr (sizeof(T) == 2) {
-    const uint2 u = *reinterpret_cast<const uint2 *>(p);
-    v[0] = bf2f((uint16_t)(u.x & 0xffffu)); v[1] = bf2f((uint16_t)(u.x >> 16));
-    v[2] = bf2f((uint16_t)(u.y & 0xffffu)); v[3] = bf2f((uint16_t)(u.y >> 16));
-  } else {
-    const float4 f = *reinterpret_cast<const float4 *>(p);
-    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-  }
-}
-
-template <typename T>
-__device__ __forceinline__ void store4(T *p, const float v[4]) {
-  if constexpr (sizeof(T) == 2) {
-    *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
-  } else {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  }
-}
-
 template <typename T, int BM, int BN, int BK, int WGM, int WGN, int LAYOUT, int EPI, bool DUAL,
           bool KCAT>
 __global__ void __launch_bounds__(WGM * WGN * 64) gemm_kernel(GemmParams p) {
@@ -183,7 +148,6 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_kernel(GemmParams p) {
   constexpr int STAGE = (BM + NB * BN) * LDK;
   constexpr bool AT = (LAYOUT == LAY_TN);
   constexpr bool BT = (LAYOUT == LAY_NT);
-  constexpr int GROUP_M = 4;
   using Frag = typename std::conditional<sizeof(T) == 2, uint4, float>::type;
   static_assert(BK % KSTEP == 0 && WTM % 16 == 0 && WTN % 16 == 0, "tile shape");
 
@@ -193,21 +157,8 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_kernel(GemmParams p) {
   const int wm = wave % WGM, wn = wave / WGM;
   const int M = p.M, N = p.N, K = p.K;
 
-  // ---- workgroup -> output tile (XCD-contiguous, then GROUP_M swizzle)
   int tm, tn;
-  {
-    const int nblk = p.tiles_m * p.tiles_n;
-    const int b = blockIdx.x;
-    const int xcd = b & 7, idx = b >> 3, base = nblk >> 3, rem = nblk & 7;
-    const int lin = xcd * base + (xcd < rem ? xcd : rem) + idx;
-    const int per_group = GROUP_M * p.tiles_n;
-    const int group = lin / per_group;
-    const int first_m = group * GROUP_M;
-    const int gsz = min(p.tiles_m - first_m, GROUP_M);
-    const int in = lin - group * per_group;
-    tm = first_m + in % gsz;
-    tn = in / gsz;
-  }
+  tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const T *__restrict__ Ag = static_cast<const T *>(p.A);
@@ -295,54 +246,12 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_kernel(GemmParams p) {
       const int col = n0 + wn * WTN + j * 16 + (lane >> 4) * 4;
       if (row >= M || col >= N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      if (p.bias != nullptr) {
-        float bv[4];
-        if constexpr (EPI == EPI_STORE_F32) load4(static_cast<const float *>(p.bias) + col, bv);
-        else load4(static_cast<const T *>(p.bias) + col, bv);
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DUAL) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] += bv[r];
+        for (int r = 0; r < 4; ++r) u[r] = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
       }
-      const int64_t rowi = row;
-      if constexpr (EPI == EPI_STORE) {
-        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, v);
-      } else if constexpr (EPI == EPI_STORE_F32) {
-        store4(static_cast<float *>(p.C) + rowi * p.ldc + col, v);
-      } else if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gelu_f(v[r]);
-        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, v);
-      } else if constexpr (EPI == EPI_SWIGLU) {
-        const float u[4] = {acc2[DUAL ? i : 0][DUAL ? j : 0][0], acc2[DUAL ? i : 0][DUAL ? j : 0][1],
-                            acc2[DUAL ? i : 0][DUAL ? j : 0][2], acc2[DUAL ? i : 0][DUAL ? j : 0][3]};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = silu_f(v[r]) * u[r];
-        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, v);
-      } else if constexpr (EPI == EPI_GELU_BWD) {
-        float dh[4], dz[4], hh[4];
-        load4(static_cast<const T *>(p.D) + rowi * p.ldd + col, dh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dz[r] = dh[r] * gelu_grad_f(v[r]);
-          hh[r] = gelu_f(v[r]);
-        }
-        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, dz);
-        store4(static_cast<T *>(p.C2) + rowi * p.ldc2 + col, hh);
-      } else if constexpr (EPI == EPI_SWIGLU_BWD) {
-        float dh[4], dzg[4], dzu[4], hh[4];
-        load4(static_cast<const T *>(p.D) + rowi * p.ldd + col, dh);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float g = v[r], u = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
-          const float sg = sigmoid_f(g);
-          const float sl = g * sg;
-          dzu[r] = dh[r] * sl;
-          dzg[r] = dh[r] * u * (sg * (1.0f + g * (1.0f - sg)));
-          hh[r] = sl * u;
-        }
-        store4(static_cast<T *>(p.C) + rowi * p.ldc + col, dzg);
-        store4(static_cast<T *>(p.C3) + rowi * p.ldc3 + col, dzu);
-        store4(static_cast<T *>(p.C2) + rowi * p.ldc2 + col, hh);
-      }
+      epilogue4<T, EPI>(p, row, col, v, u);
     }
   }
 }
@@ -418,7 +327,11 @@ static hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.dtype == DT_BF16) return dispatch<uint16_t>(a, s);
+  if (a.dtype == DT_BF16) {
+    const hipError_t e = launch_gemm_lds(a, s);
+    if (e != hipErrorNotSupported) return e;
+    return dispatch<uint16_t>(a, s);
+  }
   if (a.dtype == DT_F32) return dispatch<float>(a, s);
   return hipErrorInvalidValue;
 }

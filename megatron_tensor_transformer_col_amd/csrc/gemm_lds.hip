@@ -1,0 +1,434 @@
+// bf16 MFMA GEMM for gfx950 fed by direct HBM -> LDS DMA.
+//
+//   C[M x N] = A[M x K] . B[K x N]   (fp32 accumulate, K a multiple of 64)
+//
+// Same operand layouts and fused epilogues as the general kernel (gemm.hip);
+// what changes is the data path, built for CDNA4:
+//
+//  * global_load_lds_dwordx4 moves each 16-byte granule straight from HBM
+//    into LDS without passing through VGPRs, so a 6-stage ring of 32-deep
+//    K-slabs can be in flight with no staging registers.  A wave's DMA
+//    writes 1 KiB of LDS contiguously (lane i -> byte 16*i); the LDS layout
+//    is chosen by which global granule each lane fetches.
+//  * Operands stored k-contiguous (A in NN/NT, B in NT) keep rows of one
+//    slab depth; fragment reads are ds_read_b128.  Granule c of row r sits
+//    at c ^ swz_k(r), which spreads the 16 rows a read touches over all
+//    banks.
+//  * Operands stored m/n-contiguous (B in NN, A and B in TN) keep the global
+//    [k][n] row layout; the MFMA operand (8 consecutive k of one column) is
+//    produced by two ds_read_b64_tr_b16 transpose reads.  Within a 16-lane
+//    group, lane j receives element (j & 3) of the 8-byte chunks addressed
+//    by lanes 4e + (j >> 2), e = 0..3; lane s therefore addresses row
+//    k0 + 8g + (s >> 2) (+4 for the second read), columns 4(s & 3) .. +3.
+//    Granule index bits 1..3 are XOR-swizzled with the row so that the 8
+//    rows a half-wave reads land on distinct banks.
+//  * One barrier per K-slab; s_waitcnt vmcnt(n) waits only for the slab
+//    about to be used while later slabs' DMA stays in flight.  The MFMA
+//    operands of slab k+1 are read from LDS into a second register set
+//    while slab k's MFMAs run (interleaved by sched_group_barrier), so LDS
+//    latency hides under matrix-core work even at one wave per SIMD.
+//  * Rows/columns past M or N are clamped to the last valid one (their
+//    results are never stored), so no load leaves the operands.
+#include <type_traits>
+
+#include "gemm_common.hpp"
+
+namespace tpcol {
+
+#define TP_AS1 __attribute__((address_space(1)))
+#define TP_AS3 __attribute__((address_space(3)))
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+// k-contiguous rows of BK elements (BK/8 granules); granule swizzle per row
+template <int BK>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
+  else return ((r >> 1) ^ (r >> 3)) & 3;
+}
+__device__ __forceinline__ int swz_mn(int r) { return ((r & 3) | (((r >> 3) & 1) << 2)) << 1; }
+
+// One wave-wide DMA: lane i's 16 bytes at g land at LDS byte address
+// lds + 16*i.  Issued as inline assembly on purpose: the compiler then does
+// not count it as a pending LDS write, so it neither drains it at every
+// barrier nor before every ds_read; the kernel orders it explicitly with
+// wait_vmcnt + barrier.
+__device__ __forceinline__ void dma16(const uint16_t *g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 const void *)p);
+}
+
+// Wait until at most N of this wave's DMA ops are still in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint2 tr_read(const uint16_t *p) {
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_AS3 i16x4_t *)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// ---------------------------------------------------------------- tile DMA
+// k-contiguous operand: ROWS rows x BK k; one wave-DMA fills 1 KiB =
+// 1024 / (2 BK) rows.
+template <int ROWS, int BK, int NW>
+struct KTileDma {
+  static constexpr int GPR = BK / 8;          // granules per row
+  static constexpr int RPB = 64 / GPR;        // rows per 1 KiB block
+  static constexpr int NBLK = ROWS / RPB;
+  static constexpr int PER_WAVE = NBLK / NW;
+  static_assert(NBLK % NW == 0, "tile rows");
+  const uint16_t *src[PER_WAVE];
+  const uint16_t *src2[PER_WAVE];
+
+  __device__ __forceinline__ void init(const uint16_t *g, int64_t ld, const uint16_t *g2, int64_t ld2,
+                                       int row0, int rows_lim, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave + NW * j;
+      const int row = blk * RPB + lane / GPR;
+      const int c = (lane % GPR) ^ swz_k<BK>(row);
+      const int64_t gr = min(row0 + row, rows_lim - 1);
+      src[j] = g + gr * ld + c * 8;
+      src2[j] = g2 ? g2 + gr * ld2 + c * 8 : nullptr;
+    }
+  }
+  // k0: first k of the slab; use2: the slab lies in the second source, whose
+  // k index starts at K1 (K1 a multiple of BK)
+  __device__ __forceinline__ void issue(uint32_t lds, int k0, int K1, bool use2, int wave) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave + NW * j;
+      const uint16_t *s = use2 ? src2[j] + (k0 - K1) : src[j] + k0;
+      dma16(s, lds + blk * 1024);
+    }
+  }
+};
+
+// m/n-contiguous operand: BK k-rows x COLS, each row COLS/8 granules.
+template <int COLS, int BK, int NW>
+struct MNTileDma {
+  static constexpr int GPR = COLS / 8;      // granules per row
+  static constexpr int RPB = 64 / GPR;      // rows per 1 KiB block
+  static constexpr int NBLK = BK / RPB;     // blocks per slab
+  static constexpr int PER_WAVE = NBLK / NW;
+  static_assert(GPR >= 16 && RPB >= 1 && NBLK % NW == 0, "MN tile needs at least 128 columns");
+  const uint16_t *src[PER_WAVE];
+  int64_t step;  // elements per slab (BK rows)
+
+  __device__ __forceinline__ void init(const uint16_t *g, int64_t ld, int col0, int col_lim, int wave,
+                                       int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave + NW * j;
+      const int row = blk * RPB + lane / GPR;
+      const int lg = (lane % GPR) ^ swz_mn(row);
+      const int col = min(col0 + lg * 8, col_lim - 8);
+      src[j] = g + (int64_t)row * ld + col;
+    }
+    step = (int64_t)BK * ld;
+  }
+  __device__ __forceinline__ void issue(uint32_t lds, int kt, int wave) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave + NW * j;
+      dma16(src[j] + kt * step, lds + blk * 1024);
+    }
+  }
+};
+
+// ---------------------------------------------------------------- fragments
+// k-contiguous tile (rows of BK): 8 k of row `row`, granule c = kc*4 + g.
+template <int BK>
+__device__ __forceinline__ uint4 frag_k(const uint16_t *t, int row, int c) {
+  return *reinterpret_cast<const uint4 *>(t + row * BK + ((c ^ swz_k<BK>(row)) << 3));
+}
+
+// m/n-contiguous tile: 8 consecutive k (kc*32 + 8g ..) of column c0 + (lane & 15).
+template <int COLS>
+__device__ __forceinline__ uint4 frag_mn(const uint16_t *t, int kc, int c0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int r1 = kc * 32 + 8 * g + (s >> 2);
+  const int col = c0 + 4 * (s & 3);
+  const int sw = swz_mn(r1);  // == swz_mn(r1 + 4)
+  const int off = (((col >> 3) ^ sw) << 3) + (col & 4);
+  const uint2 a = tr_read(t + r1 * COLS + off);
+  const uint2 b = tr_read(t + (r1 + 4) * COLS + off);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
+
+// BM x BN tile per workgroup of WGM x WGN wave64s; LBK-deep K slabs through a
+// STAGES-deep LDS ring.  PREFETCH: read the next slab's fragments while the
+// current slab's MFMAs run (for one wave per SIMD); without it the second
+// wave on each SIMD covers the LDS latency.
+template <int BM, int BN, int LBK, int WGM, int WGN, int LAYOUT, int EPI, bool DUAL, bool KCAT,
+          int STAGES, bool PREFETCH>
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr bool AT = (LAYOUT == LAY_TN);
+  constexpr bool BT = (LAYOUT == LAY_NT);
+  constexpr int NB = DUAL ? 2 : 1;
+  constexpr int A_EL = BM * LBK, B_EL = BN * LBK;
+  constexpr int STAGE = A_EL + NB * B_EL;
+  using ATile = typename std::conditional<AT, MNTileDma<BM, LBK, NW>, KTileDma<BM, LBK, NW>>::type;
+  using BTile = typename std::conditional<BT, KTileDma<BN, LBK, NW>, MNTileDma<BN, LBK, NW>>::type;
+  constexpr int LOADS = ATile::PER_WAVE + NB * BTile::PER_WAVE;  // DMA ops per wave per slab
+  static_assert(STAGES >= 2 && LOADS * (STAGES - 1) < 64, "pipeline depth");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int M = p.M, N = p.N;
+  const int nk = p.K / LBK;
+
+  int tm, tn;
+  tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint16_t *Ag = static_cast<const uint16_t *>(p.A);
+  const uint16_t *Bg = static_cast<const uint16_t *>(p.B);
+  const uint16_t *B2g = static_cast<const uint16_t *>(p.B2);
+
+  ATile ta;
+  BTile tb;
+  MNTileDma<BN, LBK, NW> tb2;
+  if constexpr (AT) ta.init(Ag, p.lda, m0, M, wave, lane);
+  else ta.init(Ag, p.lda, nullptr, 0, m0, M, wave, lane);
+  if constexpr (BT) tb.init(Bg, p.ldb, KCAT ? B2g : nullptr, p.ldb2, n0, N, wave, lane);
+  else tb.init(Bg, p.ldb, n0, N, wave, lane);
+  if constexpr (DUAL) tb2.init(B2g, p.ldb2, n0, N, wave, lane);
+
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int kt, int stage) {
+    const uint32_t base = smem_lds + stage * (STAGE * 2);
+    if constexpr (AT) ta.issue(base, kt, wave);
+    else ta.issue(base, kt * LBK, 0, false, wave);
+    if constexpr (BT) {
+      const int k0 = kt * LBK;
+      tb.issue(base + A_EL * 2, k0, p.K1, KCAT && k0 >= p.K1, wave);
+    } else {
+      tb.issue(base + A_EL * 2, kt, wave);
+    }
+    if constexpr (DUAL) tb2.issue(base + (A_EL + B_EL) * 2, kt, wave);
+  };
+
+  f32x4_t acc[TM][TN];
+  f32x4_t acc2[DUAL ? TM : 1][DUAL ? TN : 1];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc2[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int g = lane >> 4, l16 = lane & 15;
+
+  // Register fragments of one whole slab (both 32-deep k chunks).
+  struct Frags {
+    uint4 a[LBK / 32][TM];
+    uint4 b[LBK / 32][TN];
+    uint4 b2[LBK / 32][DUAL ? TN : 1];
+  };
+  auto load_frags = [&](Frags &F, int stage) {
+    const uint16_t *As = smem + stage * STAGE;
+    const uint16_t *Bs = As + A_EL;
+    const uint16_t *B2s = Bs + B_EL;
+#pragma unroll
+    for (int kc = 0; kc < LBK / 32; ++kc) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        if constexpr (AT) F.a[kc][i] = frag_mn<BM>(As, kc, wm * WTM + i * 16, lane);
+        else F.a[kc][i] = frag_k<LBK>(As, wm * WTM + i * 16 + l16, kc * 4 + g);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if constexpr (BT) F.b[kc][j] = frag_k<LBK>(Bs, wn * WTN + j * 16 + l16, kc * 4 + g);
+        else F.b[kc][j] = frag_mn<BN>(Bs, kc, wn * WTN + j * 16, lane);
+        if constexpr (DUAL) F.b2[kc][j] = frag_mn<BN>(B2s, kc, wn * WTN + j * 16, lane);
+      }
+    }
+  };
+  auto mma = [&](const Frags &F) {
+#pragma unroll
+    for (int kc = 0; kc < LBK / 32; ++kc) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(F.b[kc][j], F.a[kc][i], acc[i][j]);
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc2[i][j] = mfma16(F.b2[kc][j], F.a[kc][i], acc2[i][j]);
+      }
+    }
+  };
+  // LDS read instructions and MFMAs per slab, for the interleave hint
+  constexpr int DS_A = (LBK / 32) * TM * (AT ? 2 : 1);
+  constexpr int DS_B = (LBK / 32) * TN * (BT ? 1 : 2) * NB;
+  constexpr int N_DS = DS_A + DS_B;
+  constexpr int N_MFMA = (LBK / 32) * TM * TN * NB;
+  constexpr int MFMA_PER_DS = (N_MFMA + N_DS - 1) / N_DS;
+
+  // One slab: MFMAs on F (already in registers) while the next slab's
+  // fragments stream from LDS into Fn.
+  auto step = [&](int kt, Frags &F, Frags &Fn) {
+    if (kt + 1 < nk) {
+      if (kt + STAGES - 1 < nk) wait_vmcnt<LOADS * (STAGES - 2)>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // slab kt+1 visible; every wave is done reading slab kt's stage
+      if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
+      load_frags(Fn, (kt + 1) % STAGES);
+      mma(F);
+#pragma unroll
+      for (int q = 0; q < N_DS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, MFMA_PER_DS, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
+      }
+    } else {
+      mma(F);
+    }
+  };
+
+  if constexpr (PREFETCH) {
+    // prologue: STAGES slabs in flight, slab 0's fragments into registers
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s, s);
+    if (nk >= STAGES) wait_vmcnt<LOADS * (STAGES - 1)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    Frags F0, F1;
+    load_frags(F0, 0);
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, F0, F1);
+      step(kt + 1, F1, F0);
+    }
+    if (kt < nk) step(kt, F0, F1);
+  } else {
+    // prologue: STAGES-1 slabs in flight.  Iteration kt waits for slab kt,
+    // and after the barrier refills the stage that held slab kt-1 with slab
+    // kt+STAGES-1 (every wave finished reading it before the barrier).
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s, s);
+    Frags F;
+    for (int kt = 0; kt < nk; ++kt) {
+      if (kt + STAGES - 2 < nk) wait_vmcnt<LOADS * (STAGES - 2)>();
+      else wait_vmcnt<0>();
+      __syncthreads();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
+      load_frags(F, kt % STAGES);
+      mma(F);
+    }
+  }
+
+  // ---- epilogue: lane holds C[row][col .. col+3] of every 16x16 tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * WTM + i * 16 + l16;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 16 + g * 4;
+      if (row >= M || col >= N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      float u[4] = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) u[r] = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
+      }
+      epilogue4<uint16_t, EPI>(p, row, col, v, u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+template <int BM, int BN, int LBK, int WGM, int WGN, int LAYOUT, int EPI, bool DUAL, bool KCAT,
+          int STAGES, bool PREFETCH>
+static hipError_t run_lds(const GemmArgs &a, hipStream_t s) {
+  GemmParams p;
+  p.A = a.A; p.lda = a.lda;
+  p.B = a.B; p.ldb = a.ldb;
+  p.B2 = a.B2; p.ldb2 = a.ldb2;
+  p.bias = a.bias;
+  p.D = a.D; p.ldd = a.ldd;
+  p.C = a.C; p.ldc = a.ldc;
+  p.C2 = a.C2; p.ldc2 = a.ldc2;
+  p.C3 = a.C3; p.ldc3 = a.ldc3;
+  p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K; p.K1 = (int)a.K1;
+  p.tiles_m = (int)((a.M + BM - 1) / BM);
+  p.tiles_n = (int)((a.N + BN - 1) / BN);
+  hipLaunchKernelGGL(
+      (gemm_lds_kernel<BM, BN, LBK, WGM, WGN, LAYOUT, EPI, DUAL, KCAT, STAGES, PREFETCH>),
+      dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WGM * WGN * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+// Tile configurations measured on MI355X (see the design notes): 8 wave64 per
+// workgroup (two per SIMD, so LDS and DMA latency of one wave hides under
+// the other's MFMAs) and 256-wide tiles to cut L2 -> CU traffic per flop.
+template <int LAYOUT, int EPI, bool DUAL, bool KCAT>
+static hipError_t pick_lds(const GemmArgs &a, hipStream_t s) {
+  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int64_t t128x256 = ((a.M + 127) / 128) * ((a.N + 255) / 256);
+  if constexpr (DUAL) {
+    if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 2, false>(a, s);
+    return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
+  } else {
+    if (t256 >= 192) return run_lds<256, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
+    if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
+    return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
+  }
+}
+
+hipError_t launch_gemm_lds(const GemmArgs &a, hipStream_t s) {
+  constexpr int LBK = 32;  // slab depth of every instantiation below
+  if (a.dtype != DT_BF16 || a.K <= 0 || a.K % LBK != 0) return hipErrorNotSupported;
+  if (a.kcat && a.K1 % LBK != 0) return hipErrorNotSupported;
+  // small problems stay on the general kernel (more, smaller tiles)
+  if (((a.M + 127) / 128) * ((a.N + 127) / 128) < 64) return hipErrorNotSupported;
+  if (a.M < 8 || a.N < 8) return hipErrorNotSupported;
+  switch (a.layout) {
+    case LAY_NN:
+      if (a.dual) {
+        if (a.epi == EPI_SWIGLU) return pick_lds<LAY_NN, EPI_SWIGLU, true, false>(a, s);
+        if (a.epi == EPI_SWIGLU_BWD) return pick_lds<LAY_NN, EPI_SWIGLU_BWD, true, false>(a, s);
+        return hipErrorNotSupported;
+      }
+      switch (a.epi) {
+        case EPI_STORE: return pick_lds<LAY_NN, EPI_STORE, false, false>(a, s);
+        case EPI_STORE_F32: return pick_lds<LAY_NN, EPI_STORE_F32, false, false>(a, s);
+        case EPI_GELU: return pick_lds<LAY_NN, EPI_GELU, false, false>(a, s);
+        case EPI_GELU_BWD: return pick_lds<LAY_NN, EPI_GELU_BWD, false, false>(a, s);
+        default: return hipErrorNotSupported;
+      }
+    case LAY_NT:
+      if (a.dual) return hipErrorNotSupported;
+      if (a.kcat) {
+        if (a.epi == EPI_STORE_F32) return pick_lds<LAY_NT, EPI_STORE_F32, false, true>(a, s);
+        return hipErrorNotSupported;
+      }
+      if (a.epi == EPI_STORE) return pick_lds<LAY_NT, EPI_STORE, false, false>(a, s);
+      if (a.epi == EPI_STORE_F32) return pick_lds<LAY_NT, EPI_STORE_F32, false, false>(a, s);
+      return hipErrorNotSupported;
+    case LAY_TN:
+      if (a.dual || a.kcat || a.epi != EPI_STORE_F32) return hipErrorNotSupported;
+      return pick_lds<LAY_TN, EPI_STORE_F32, false, false>(a, s);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace tpcol

@@ -67,8 +67,8 @@ def test_gemv_matches_gemm_path_and_oracle(M):
     assert_close(host(Hm), ref, "bf16", "H gemm")
 
 
-def test_gemv_repeated_calls_reset_counters():
-    # the split-K arrival counters must be left at zero for the next call
+def test_gemv_repeated_calls():
+    # split-K partials live in a shared workspace: back-to-back calls must not see stale data
     note("gemv repeated")
     rng = np.random.default_rng(0)
     X = rng.integers(-2, 3, size=(16, 2048)).astype(np.float32)

@@ -42,7 +42,9 @@ def test_col_linear_identity_act_exact(dtype, M, K, N):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,K,N", [(5, 16, 8), (129, 200, 136), (1024, 1032, 520), (4096, 256, 1024)])
+@pytest.mark.parametrize("M,K,N", [(5, 16, 8), (129, 200, 136), (1024, 1032, 520), (4096, 256, 1024),
+                                   # K % 64 == 0 and >= 64 tiles: the LDS-DMA kernel, ragged M / N
+                                   (1000, 640, 1352), (3000, 1024, 2056), (8192, 64, 1024)])
 def test_row_partial_exact(dtype, M, K, N):
     note(f"row NN exact {dtype} {M}x{K}x{N}")
     rng = np.random.default_rng(7 * M + K)

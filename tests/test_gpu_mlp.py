@@ -126,7 +126,9 @@ def test_mlp_gelu_bf16_medium(T_, h, ffn, n):
     assert_close(host(Y), ref["Y"], "bf16", "Y")
 
 
-@pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (1030, 512, 1024, 1)])
+@pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (1030, 512, 1024, 1),
+                                        # token count % 64 == 0: every GEMM on the LDS-DMA kernel
+                                        (1024, 1024, 2048, 2)])
 def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     note(f"bf16 MLP GELU bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_mlp_inputs(T_, h, ffn, "bf16", seed=2, with_dy=True, with_bias=True)
@@ -141,7 +143,7 @@ def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     assert_close(host(dX), ref["dX"], "bf16", "dX")
 
 
-@pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (520, 256, 2048, 1)])
+@pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (520, 256, 2048, 1), (1024, 1024, 2048, 2)])
 def test_mlp_swiglu_bf16_medium(T_, h, ffn, n):
     note(f"bf16 SwiGLU fwd+bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_swiglu_inputs(T_, h, ffn, "bf16", seed=3, with_dy=True)
