@@ -13,11 +13,12 @@ bf16 storage, fp32 accumulation, seeded synthetic N(0,1) activations and
 N(0, 0.02^2) weights.  value = algorithmic TFLOP/s of the whole step
 (8 GEMMs x 2*T*h*ffn/N flops) with inputs resident in HBM.
 
-The JSON line also carries: the roofline of the dominant kernel (the column
-GEMM, timed with HIP events around each launch on the launch stream), the
-fp64 CPU oracle timed on this host as a baseline, and per-row figures for the
-other workloads (SwiGLU forward/backward, head-sharded attention, decode
-GEMV) unless --no-rows.
+The step's nine launches are captured once in a HIP graph and replayed for
+the timed steps.  The JSON line also carries: the roofline of the dominant
+kernel (the column GEMM + GELU, timed with HIP events over back-to-back
+launches on the launch stream), the fp64 CPU oracle timed on this host as a
+baseline, and per-row figures for the other workloads (SwiGLU forward /
+backward, head-sharded attention, decode GEMV) unless --no-rows.
 """
 import argparse
 import json
@@ -130,11 +131,43 @@ class Headline:
         self.total()
 
 
+def graph_of(torch, fn):
+    """Capture one call of fn (library launches on the current stream) in a HIP graph."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def back_to_back_ms(torch, fn, iters):
+    """Average GPU time per launch of fn over iters back-to-back launches
+    (HIP events on torch's current stream, which is the launch stream)."""
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / iters
+
+
 def headline(torch, tp, synth, steps, warmup):
+    """One step = the 9 launches of the 4-shard MLP layer + shard sum, replayed
+    as a HIP graph (no host launch gaps between the kernels)."""
     hl = Headline(torch, tp, synth)
-    ms, kt = timed(torch, hl.step, steps, warmup)
+    for _ in range(warmup):
+        hl.step(None)
+    g = graph_of(torch, lambda: hl.step(None))
+    ms, _ = timed(torch, lambda kt: g.replay(), steps, 2)
     step_flops = 2 * hl.n * hl.gemm_flops
-    col_ms = kt.mean_ms()
+    col_ms = back_to_back_ms(torch, lambda: hl.col(0), max(steps, 50))
     return {
         "ms": ms, "tflops": step_flops / (ms * 1e-3) / 1e12, "step_flops": step_flops,
         "col_ms": col_ms, "col_tflops": hl.gemm_flops / (col_ms * 1e-3) / 1e12,
@@ -142,7 +175,7 @@ def headline(torch, tp, synth, steps, warmup):
         "config": {"workload": "gpt2m_mlp_bf16: TP MLP layer, tokens 8x1024, h 1024, ffn 4096, "
                                "4 shards in sequence + shard sum",
                    "tokens": hl.T, "h": hl.h, "ffn": hl.W.ffn, "n_shards": hl.n,
-                   "activation": "gelu_erf"},
+                   "activation": "gelu_erf", "timing": "HIP graph replay of the 9-launch step"},
     }
 
 
@@ -237,8 +270,10 @@ def rows(torch, tp, steps, warmup):
     s_ms = min(steps, 20)
     w_ms = min(warmup, 3)
     s = R.swiglu()
-    ms_f, _ = timed(torch, lambda kt: (R.swiglu_col(s), R.swiglu_down(s)), s_ms, w_ms)
-    ms_b, _ = timed(torch, lambda kt: R.swiglu_bwd(s), s_ms, w_ms)
+    gf = graph_of(torch, lambda: (R.swiglu_col(s), R.swiglu_down(s)))
+    gb = graph_of(torch, lambda: R.swiglu_bwd(s))
+    ms_f, _ = timed(torch, lambda kt: gf.replay(), s_ms, w_ms)
+    ms_b, _ = timed(torch, lambda kt: gb.replay(), s_ms, w_ms)
     flop_f, flop_b = 3 * s["flop_gemm"], 6 * s["flop_gemm"]
     out["llama_swiglu_fwd"] = {"ms": ms_f, "tflops": flop_f / ms_f / 1e9,
                                "frac_peak": flop_f / ms_f / 1e9 / PEAK_BF16_TFLOPS}
@@ -248,20 +283,16 @@ def rows(torch, tp, steps, warmup):
                                        "(+2 GEMMs) is not counted"}
     del s
     s = R.mha()
-    ms_a, _ = timed(torch, lambda kt: R.attn(s), s_ms, w_ms)
+    ga = graph_of(torch, lambda: R.attn(s))
+    ms_a, _ = timed(torch, lambda kt: ga.replay(), s_ms, w_ms)
     fa = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
     out["mha_heads_shard"] = {"ms": ms_a, "tflops": fa / ms_a / 1e9,
                               "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
                               "note": "QKV GEMM + causal attention (4*d*s(s+1)/2 per head) + W_o GEMM"}
     del s
     s = R.decode()
-    for _ in range(3):
-        R.decode_step(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        R.decode_step(s)
-    ms_d, _ = timed(torch, lambda kt: graph.replay(), s_ms, 3)
+    gd = graph_of(torch, lambda: R.decode_step(s))
+    ms_d, _ = timed(torch, lambda kt: gd.replay(), s_ms, 3)
     w_bytes = s["n"] * 2 * s["w_bytes"]
     out["decode_gemv"] = {"ms_step": ms_d, "weight_bytes": w_bytes,
                           "gbs": w_bytes / ms_d / 1e6, "frac_hbm_peak": w_bytes / ms_d / 1e6 / PEAK_HBM_GBS,
@@ -273,7 +304,13 @@ def rows(torch, tp, steps, warmup):
 # --------------------------------------------------------------------------- single ops
 def run_op(torch, tp, synth, name, iters):
     """Run one op `iters` times after a warm-up and print its mean time."""
-    if name.startswith("c2_"):
+    if name == "copy":
+        # plain device copy of a known size (256 MiB), to calibrate the HBM
+        # byte counters: FETCH_SIZE / WRITE_SIZE should each read 256 MiB
+        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+    elif name.startswith("c2_"):
         hl = Headline(torch, tp, synth)
         fn = {"c2_col": lambda: hl.col(0), "c2_row": lambda: hl.row(0), "c2_sum": hl.total,
               "c2_step": lambda: hl.step(None)}[name]
@@ -366,7 +403,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(hl["ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": hl["config"],
-        "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU epilogue (gemm_lds_kernel NN)",
+        "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU epilogue (gemm_lds_kernel NN, 128x256 tile)",
                      "achieved": round(hl["col_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(hl["col_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": None, "avg_launch_us": round(hl["col_ms"] * 1e3, 3),
