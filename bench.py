@@ -305,9 +305,10 @@ def rows(torch, tp, steps, warmup):
 def run_op(torch, tp, synth, name, iters):
     """Run one op `iters` times after a warm-up and print its mean time."""
     if name == "copy":
-        # plain device copy of a known size (256 MiB), to calibrate the HBM
-        # byte counters: FETCH_SIZE / WRITE_SIZE should each read 256 MiB
-        src = torch.empty(64 << 20, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        # plain device copy of a known size (1 GiB, four times the 256 MiB
+        # last-level cache), to calibrate the HBM byte counters:
+        # FETCH_SIZE / WRITE_SIZE should each read 1 GiB per copy
+        src = torch.empty(256 << 20, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)
     elif name.startswith("c2_"):

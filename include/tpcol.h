@@ -127,7 +127,8 @@ size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t
  *   P    [b*s x h]                      ldp    float32 (output)
  *   ws   tp_attn_heads_shard_workspace() bytes: QKV_i [b*s x 3*hl*d] then
  *        O_i [b*s x hl*d], both bf16 row-major, readable after the call.
- * Only TP_BF16 and d == 128 are supported (TP_ERR_DTYPE / TP_ERR_SHAPE).
+ * Only TP_BF16 and d == 128 are supported (TP_ERR_DTYPE / TP_ERR_SHAPE);
+ * 3*heads_local*d must not exceed 2^24 (TP_ERR_SHAPE).
  */
 int tp_attn_heads_shard(int dtype, int64_t b, int64_t s, int64_t h,
                         int64_t heads_local, int64_t d, int causal,

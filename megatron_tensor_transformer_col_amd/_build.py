@@ -26,6 +26,11 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
+# per-source additions: the attention kernel keeps its MFMA accumulators in
+# ordinary VGPRs (its softmax reads and rescales them every key block)
+EXTRA_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -53,7 +58,7 @@ def build(verbose: bool = False) -> str:
         for src in sources:
             obj = os.path.join(BUILD, src[:-4] + ".o")
             objs.append(obj)
-            cmd = [hipcc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *HIPCC_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd))
         for j in jobs:
             out = j.result()

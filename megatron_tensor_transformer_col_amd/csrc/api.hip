@@ -289,6 +289,9 @@ int tp_attn_heads_shard(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t 
   const int64_t T = b * s_len;
   if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
   const int64_t w = heads_local * d;
+  if (3 * w > (int64_t(1) << 24))
+    return fail(TP_ERR_SHAPE, "heads_local %lld too large (3*heads_local*d must be <= 2^24)",
+                (long long)heads_local);
   TRY(check_mat(X, T, h, ldx, 2, "X"));
   TRY(check_mat(Wqkv, h, 3 * w, ldwqkv, 2, "Wqkv"));
   TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));

@@ -32,12 +32,9 @@
 #include <type_traits>
 
 #include "gemm_common.hpp"
+#include "lds_dma.hpp"
 
 namespace tpcol {
-
-#define TP_AS1 __attribute__((address_space(1)))
-#define TP_AS3 __attribute__((address_space(3)))
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 // k-contiguous rows of BK elements (BK/8 granules); granule swizzle per row
 template <int BK>
@@ -46,31 +43,6 @@ __device__ __forceinline__ int swz_k(int r) {
   else return ((r >> 1) ^ (r >> 3)) & 3;
 }
 __device__ __forceinline__ int swz_mn(int r) { return ((r & 3) | (((r >> 3) & 1) << 2)) << 1; }
-
-// One wave-wide DMA: lane i's 16 bytes at g land at LDS byte address
-// lds + 16*i.  Issued as inline assembly on purpose: the compiler then does
-// not count it as a pending LDS write, so it neither drains it at every
-// barrier nor before every ds_read; the kernel orders it explicitly with
-// wait_vmcnt + barrier.
-__device__ __forceinline__ void dma16(const uint16_t *g, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
-  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 const void *)p);
-}
-
-// Wait until at most N of this wave's DMA ops are still in flight.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint2 tr_read(const uint16_t *p) {
-  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_AS3 i16x4_t *)(p));
-  return __builtin_bit_cast(uint2, v);
-}
 
 // ---------------------------------------------------------------- tile DMA
 // k-contiguous operand: ROWS rows x BK k; one wave-DMA fills 1 KiB =
