@@ -61,13 +61,6 @@ static constexpr int FA_ROWS_J = 4 * FA_NW;    // tile rows between one wave's D
 static constexpr float FA_RESCALE_LOG2 = 8.0f;
 static constexpr int64_t FA_MAX_LD = int64_t(1) << 24;  // keeps 64 rows' byte offsets in 32 bits
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf2_hw(float lo, float hi) {
-  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even
-  return __builtin_bit_cast(uint32_t, v);
-}
-
 // Butterfly steps across lanes i and i ^ 16 / i ^ 32 with the gfx950 row
 // swaps: after v_permlane{16,32}_swap of a register with itself, one of the
 // two results holds the lane's own value and the other its partner's.
@@ -265,9 +258,9 @@ struct FaBlock {
           }
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc)
-          pf[qt][kc] = make_uint4(pack_bf2_hw(p[2 * kc][0], p[2 * kc][1]), pack_bf2_hw(p[2 * kc][2], p[2 * kc][3]),
-                                  pack_bf2_hw(p[2 * kc + 1][0], p[2 * kc + 1][1]),
-                                  pack_bf2_hw(p[2 * kc + 1][2], p[2 * kc + 1][3]));
+          pf[qt][kc] = make_uint4(pack_bf2(p[2 * kc][0], p[2 * kc][1]), pack_bf2(p[2 * kc][2], p[2 * kc][3]),
+                                  pack_bf2(p[2 * kc + 1][0], p[2 * kc + 1][1]),
+                                  pack_bf2(p[2 * kc + 1][2], p[2 * kc + 1][3]));
       }
     };
 
@@ -342,7 +335,7 @@ struct FaBlock {
           const f32x4_t v = (o[qt][dt] * a0 + o1 * a1) * inv;
           if (q < a.s)
             *reinterpret_cast<uint2 *>(orow + dt * 16 + 4 * g) =
-                make_uint2(pack_bf2_hw(v[0], v[1]), pack_bf2_hw(v[2], v[3]));
+                make_uint2(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]));
         }
       }
     }

@@ -14,17 +14,14 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // bf16 values travel as raw uint16_t patterns.
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// float -> bf16 with round-to-nearest-even (NaN kept quiet).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
+// float -> bf16, round to nearest even, by the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32 converts two values per instruction; NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> {

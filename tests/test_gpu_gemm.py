@@ -121,3 +121,31 @@ def test_repeat_runs_are_bitwise_identical():
     torch().cuda.synchronize()
     for h in outs[1:]:
         assert torch().equal(h, outs[0])
+
+
+@pytest.mark.parametrize("M,K,N", [(37, 24, 40), (8, 1024, 1032), (2048, 64, 2048), (1000, 640, 1352)])
+def test_bf16_output_rounding_nearest_even(M, K, N):
+    """bf16 outputs are the exact fp32 sums rounded to nearest, ties to even.
+
+    Integer operands up to 60 in magnitude give exact sums of 9-17 bits, so
+    most outputs need rounding to bf16's 8 significant bits and many land
+    exactly on a tie; every output's bits must equal the CPU rounding of
+    the exact sum (general and LDS-DMA kernels, and the decode GEMV)."""
+    note(f"bf16 rounding {M}x{K}x{N}")
+    rng = np.random.default_rng(3 * M + N)
+    X = rng.integers(-60, 61, size=(M, K)).astype(np.float32)
+    W = rng.integers(-4, 5, size=(K, N)).astype(np.float32)
+    exact = (X.astype(np.int64) @ W.astype(np.int64)).astype(np.float32)
+    want = synth.round_to_bf16_bits(exact)
+    ties = np.count_nonzero((exact.view(np.uint32) & 0xFFFF) == 0x8000)
+    assert ties > 0 or M * N < 4096
+    for gemv_max in (0, 16):
+        H = empty((M, N), "bf16")
+        prev = tp.tp_set_gemv_max_m(gemv_max)
+        try:
+            tp.tp_col_linear_gelu(dev(_as("bf16", X)), dev(_as("bf16", W)), H, act="none")
+        finally:
+            tp.tp_set_gemv_max_m(prev)
+        torch().cuda.synchronize()
+        got = H.view(torch().int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), (gemv_max, int(np.count_nonzero(got != want)))
