@@ -8,17 +8,20 @@
 //
 //  * Workgroup = 4 wave64 over a 64-column strip of W and one K range
 //    (split-K across workgroups so that a 3584 x 8192 or 8192 x 3584 shard
-//    still spreads over all 256 CUs).  The K range of x (16 x Krange, zero
-//    padded past M and K) is staged once in LDS.
-//  * W streams HBM -> LDS with global_load_lds_dwordx4 (no VGPR staging) in
-//    64-row slabs through a 4-deep ring (128-byte row segments); a slab is
-//    8 KiB, two DMA ops per wave.
+//    spreads over all 256 CUs, two workgroups per CU).
+//  * Each ring stage holds a 64-row slab of the strip (8 KiB) and the
+//    matching 16 x 64 slice of x (2 KiB); both move HBM -> LDS with
+//    global_load_lds_dwordx4 (no VGPR staging), three DMA ops per wave per
+//    stage, through a 7-deep ring: six stages (60 KiB) stay in flight per
+//    workgroup, enough to cover HBM latency at full bandwidth.
 //  * Each wave owns 16 of the 64 columns.  The MFMA B operand (8 consecutive
 //    k of one column) comes from ds_read_b64_tr_b16 transpose reads of the
-//    [k][n] slab, the A operand from the x slice (ds_read_b128), and
-//    v_mfma_f32_16x16x32_bf16 does the work, M padded to 16 with zeros.
-//  * Rows past K read a clamped (valid) weight row against zero x, so they
-//    add nothing; columns past N are clamped and never stored.
+//    [k][n] slab, the A operand (x) from ds_read_b128, and
+//    v_mfma_f32_16x16x32_bf16 does the work.  Token rows past M read the
+//    last valid row (their results are never stored).
+//  * A ragged K tail (the last slab of the last split) reads W rows clamped
+//    to K-1 against a zero-padded copy of x built in registers, so those
+//    rows add nothing and no load leaves x.
 //  * Partial sums go to an fp32 workspace [splits][16][N]; a second small
 //    kernel adds them in split order, adds the bias and applies the
 //    activation.  The activation must come after the full K reduction
@@ -26,18 +29,19 @@
 //    No workgroup waits on another and nothing has to be pre-zeroed.
 #include "device_common.hpp"
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 
 namespace tpcol {
 
-#define TP_AS3 __attribute__((address_space(3)))
-typedef short gv_i16x4_t __attribute__((ext_vector_type(4)));
-
-static constexpr int GV_BN = 64;       // columns per workgroup strip
-static constexpr int GV_SLAB = 64;     // k rows per LDS slab
-static constexpr int GV_STAGES = 4;    // slab ring depth
-static constexpr int GV_NT = 256;      // 4 wave64
-static constexpr int GV_MAX_KR = 1024; // max K range per workgroup (x slice in LDS)
+static constexpr int GV_BN = 64;        // columns per workgroup strip
+static constexpr int GV_SLAB = 64;      // k rows per slab
+static constexpr int GV_STAGES = 7;     // ring depth
+static constexpr int GV_NT = 256;       // 4 wave64
 static constexpr int GV_TARGET_WG = 512;
+static constexpr int GV_WSLAB = GV_SLAB * GV_BN;  // W elements per stage (8 KiB)
+static constexpr int GV_XSLAB = 16 * GV_SLAB;     // x elements per stage (2 KiB)
+static constexpr int GV_STAGE = GV_WSLAB + GV_XSLAB;
+static constexpr int GV_DMA = 3;                  // DMA ops per wave per stage (2 W + 1 x)
 
 struct GvPlan {
   int strips, splits, krange;
@@ -47,9 +51,9 @@ static GvPlan gv_plan(int64_t K, int64_t N) {
   GvPlan p;
   p.strips = (int)((N + GV_BN - 1) / GV_BN);
   const int64_t kslabs = (K + GV_SLAB - 1) / GV_SLAB;
-  int64_t splits = (GV_TARGET_WG + p.strips - 1) / p.strips;
-  const int64_t min_splits = (kslabs * GV_SLAB + GV_MAX_KR - 1) / GV_MAX_KR;
-  if (splits < min_splits) splits = min_splits;
+  // all workgroups in one wave of the launch (a partial second wave would
+  // double the time): at most GV_TARGET_WG of them
+  int64_t splits = GV_TARGET_WG / p.strips;
   if (splits > kslabs) splits = kslabs;
   if (splits < 1) splits = 1;
   const int64_t slabs_per = (kslabs + splits - 1) / splits;
@@ -66,42 +70,9 @@ size_t gemv_workspace(int64_t K, int64_t N) {
 
 int64_t gemv_max_n() { return (int64_t)1 << 30; }
 
-__device__ __forceinline__ void gv_dma16(const uint16_t *g, uint16_t *lds_wave_base) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 void *)lds_wave_base);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void gv_wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
 // 64-column slab rows (8 granules): granule index bits 1..2 swizzled so that
 // the 8 rows one half-wave transposes land on distinct banks.
 __device__ __forceinline__ int gv_swz(int r) { return (((r >> 1) & 1) | (((r >> 3) & 1) << 1)) << 1; }
-
-template <int EPI>
-__device__ __forceinline__ void gv_store8(float v[8], const uint16_t *bias, int col, void *Y,
-                                          int64_t ldy, int m) {
-  if (bias != nullptr) {
-    const uint4 b = *reinterpret_cast<const uint4 *>(bias + col);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] += bf2f((uint16_t)(u4_word(b, j >> 1) >> ((j & 1) * 16)));
-  }
-  if constexpr (EPI == EPI_STORE_F32) {
-    float *y = static_cast<float *>(Y) + (int64_t)m * ldy + col;
-    *reinterpret_cast<float4 *>(y) = make_float4(v[0], v[1], v[2], v[3]);
-    *reinterpret_cast<float4 *>(y + 4) = make_float4(v[4], v[5], v[6], v[7]);
-  } else {
-    if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = gelu_f(v[j]);
-    }
-    uint16_t *y = static_cast<uint16_t *>(Y) + (int64_t)m * ldy + col;
-    *reinterpret_cast<uint4 *>(y) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
-                                               pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
-  }
-}
 
 // FINAL: single split, apply the epilogue directly; else write fp32 partials.
 template <int EPI, bool FINAL>
@@ -109,9 +80,8 @@ __global__ void __launch_bounds__(GV_NT)
 gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const uint16_t *__restrict__ W,
                     int64_t ldw, int K, int N, int krange, const uint16_t *bias, void *Y,
                     int64_t ldy, float *part) {
-  constexpr int XLD = GV_MAX_KR + 8;  // padded x row (16 B pad: conflict-free b128 reads)
-  __shared__ __attribute__((aligned(1024))) uint16_t slab[GV_STAGES][GV_SLAB * GV_BN];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[16 * XLD];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[GV_STAGES * GV_STAGE + GV_XSLAB];
+  uint16_t *xtail = smem + GV_STAGES * GV_STAGE;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,10 +91,13 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   const int k_begin = split * krange;
   const int k_end = min(K, k_begin + krange);
   const int nslab = (k_end - k_begin + GV_SLAB - 1) / GV_SLAB;
+  const int tail = ((k_end - k_begin) % GV_SLAB) ? nslab - 1 : -1;  // slab with rows past K
 
-  // ---- DMA sources: per slab 8 blocks of 8 rows x 8 granules; wave w owns
-  //      blocks w and w + 4.  Lane i of a block fetches row i/8, granule
-  //      (i%8) ^ swz(row), clamped into the matrix.
+  // ---- DMA sources.  W: per slab 8 blocks of 8 rows x 8 granules; wave w
+  //      owns blocks w and w + 4; lane i of a block fetches row i/8, granule
+  //      (i%8) ^ swz(row), clamped into the matrix.  x: wave w fetches token
+  //      rows 4w .. 4w+3 (lanes 0..31), granule (i%8) ^ (row & 7), token rows
+  //      past M clamped to M-1.
   int col_of[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
@@ -132,29 +105,40 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
     const int lg = (lane & 7) ^ gv_swz(row);
     col_of[j] = min(n0 + lg * 8, N - 8);
   }
+  const int xrow = 4 * wave + ((lane >> 3) & 3);
+  const uint16_t *xrow_ptr = X + (int64_t)min(xrow, M - 1) * ldx;
+  const int xgran = ((lane & 7) ^ (xrow & 7)) * 8;
+  const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int s) {
     const int kr = k_begin + s * GV_SLAB;
-    uint16_t *base = slab[s % GV_STAGES];
+    const uint32_t base = lds0 + (uint32_t)((s % GV_STAGES) * GV_STAGE * 2);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // rows past K are clamped to K-1: valid memory, multiplied by zero x
+      // rows past K are clamped to K-1: valid memory, matched by zero x
       const int row = min(kr + (wave + 4 * j) * 8 + (lane >> 3), K - 1);
-      gv_dma16(W + (int64_t)row * ldw + col_of[j], base + (wave + 4 * j) * 512);
+      dma16(W + (int64_t)row * ldw + col_of[j], base + (wave + 4 * j) * 1024);
     }
+    // the tail slab's x comes from xtail; its DMA re-reads the first 8
+    // elements of the row (valid for any K) so every wave issues the same
+    // number of ops per stage
+    const uint16_t *xs = (s == tail) ? xrow_ptr : xrow_ptr + kr + xgran;
+    if (lane < 32) dma16(xs, base + GV_WSLAB * 2 + wave * 512);
   };
-  // ---- x slice -> LDS (zero past M and past K)
-  const int kv = nslab * (GV_SLAB / 8);  // 16-byte vectors per x row
-  for (int v = tid; v < 16 * kv; v += GV_NT) {
-    const int m = v / kv, kk = (v % kv) * 8;
-    const int k = k_begin + kk;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (m < M && k < K) val = *reinterpret_cast<const uint4 *>(X + (int64_t)m * ldx + k);
-    *reinterpret_cast<uint4 *>(&xs[m * XLD + kk]) = val;
-  }
 
+  // ---- prologue: STAGES-1 slabs in flight, then the zero-padded tail of x
 #pragma unroll
   for (int s = 0; s < GV_STAGES - 1; ++s)
     if (s < nslab) issue(s);
+  if (tail >= 0) {
+    // 16 rows x 64 k, 8 elements per thread (threads 0..127), zero past M / K
+    if (tid < 128) {
+      const int m = tid >> 3, c = tid & 7;
+      const int k = k_begin + tail * GV_SLAB + c * 8;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (m < M && k < K) v = *reinterpret_cast<const uint4 *>(X + (int64_t)m * ldx + k);
+      *reinterpret_cast<uint4 *>(xtail + m * GV_SLAB + ((c ^ (m & 7)) << 3)) = v;
+    }
+  }
 
   // ---- stream the slabs
   f32x4_t acc = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -162,22 +146,20 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   const int s4 = l16 >> 2;
   const int colw = cw + 4 * (l16 & 3);
   for (int s = 0; s < nslab; ++s) {
-    if (s + GV_STAGES - 2 < nslab) gv_wait_vmcnt<2 * (GV_STAGES - 2)>();
-    else gv_wait_vmcnt<0>();
-    __syncthreads();
+    if (s + GV_STAGES - 2 < nslab) wait_vmcnt<GV_DMA * (GV_STAGES - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // slab s visible to all; every wave is done with slab s-1's stage
     if (s + GV_STAGES - 1 < nslab) issue(s + GV_STAGES - 1);
-    const uint16_t *t = slab[s % GV_STAGES];
+    const uint16_t *t = smem + (s % GV_STAGES) * GV_STAGE;
+    const uint16_t *xt = (s == tail) ? xtail : t + GV_WSLAB;
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
       const int r1 = kc * 32 + 8 * g + s4;
       const int off = (((colw >> 3) ^ gv_swz(r1)) << 3) + (colw & 4);
-      const gv_i16x4_t b0 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_AS3 gv_i16x4_t *)(t + r1 * GV_BN + off));
-      const gv_i16x4_t b1 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((TP_AS3 gv_i16x4_t *)(t + (r1 + 4) * GV_BN + off));
-      const uint2 u0 = __builtin_bit_cast(uint2, b0), u1 = __builtin_bit_cast(uint2, b1);
+      const uint2 u0 = tr_read(t + r1 * GV_BN + off);
+      const uint2 u1 = tr_read(t + (r1 + 4) * GV_BN + off);
       const uint4 bf = make_uint4(u0.x, u0.y, u1.x, u1.y);
-      const uint4 af = *reinterpret_cast<const uint4 *>(&xs[l16 * XLD + s * GV_SLAB + kc * 32 + g * 8]);
+      const uint4 af = *reinterpret_cast<const uint4 *>(xt + l16 * GV_SLAB + (((kc * 4 + g) ^ (l16 & 7)) << 3));
       acc = mfma16(bf, af, acc);  // lane: token l16, columns cw + 4g .. +3
     }
   }
@@ -210,24 +192,43 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   }
 }
 
-// Y[m][c..c+7] = epi(sum_s part[s][m][c..c+7] + bias), splits added in order.
+// Y[m][c..c+3] = epi(sum_s part[s][m][c..c+3] + bias), splits added in order.
 template <int EPI>
 __global__ void __launch_bounds__(256)
 gemv_finalize_kernel(const float *__restrict__ part, int splits, int M, int N,
                      const uint16_t *bias, void *Y, int64_t ldy) {
-  const int n8 = N / 8;
+  const int n4 = N / 4;
   const int v = blockIdx.x * 256 + threadIdx.x;
-  if (v >= M * n8) return;
-  const int m = v / n8, col = (v % n8) * 8;
-  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < splits; ++sp) {
-    const float *p = part + ((int64_t)sp * 16 + m) * N + col;
-    const float4 a = *reinterpret_cast<const float4 *>(p);
-    const float4 b = *reinterpret_cast<const float4 *>(p + 4);
-    s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-    s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+  if (v >= M * n4) return;
+  const int m = v / n4, col = (v % n4) * 4;
+  const float *p = part + (int64_t)m * N + col;
+  const int64_t step = (int64_t)16 * N;
+  f32x4_t s = *reinterpret_cast<const f32x4_t *>(p);
+  int sp = 1;
+  for (; sp + 4 <= splits; sp += 4) {  // four loads in flight, added in split order
+    const f32x4_t a = *reinterpret_cast<const f32x4_t *>(p + sp * step);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t *>(p + (sp + 1) * step);
+    const f32x4_t c = *reinterpret_cast<const f32x4_t *>(p + (sp + 2) * step);
+    const f32x4_t d = *reinterpret_cast<const f32x4_t *>(p + (sp + 3) * step);
+    s += a; s += b; s += c; s += d;
   }
-  gv_store8<EPI>(s, bias, col, Y, ldy, m);
+  for (; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t *>(p + sp * step);
+  float r[4] = {s[0], s[1], s[2], s[3]};
+  if (bias != nullptr) {
+    const uint2 b = *reinterpret_cast<const uint2 *>(bias + col);
+    r[0] += bf2f((uint16_t)(b.x & 0xffffu)); r[1] += bf2f((uint16_t)(b.x >> 16));
+    r[2] += bf2f((uint16_t)(b.y & 0xffffu)); r[3] += bf2f((uint16_t)(b.y >> 16));
+  }
+  if constexpr (EPI == EPI_STORE_F32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(Y) + (int64_t)m * ldy + col) = make_float4(r[0], r[1], r[2], r[3]);
+  } else {
+    if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = gelu_f(r[j]);
+    }
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + (int64_t)m * ldy + col) =
+        make_uint2(pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3]));
+  }
 }
 
 template <int EPI>
@@ -247,7 +248,7 @@ static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
                      (int)a.M, W, a.ldw, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int total = (int)a.M * (int)(a.N / 8);
+  const int total = (int)a.M * (int)(a.N / 4);
   hipLaunchKernelGGL((gemv_finalize_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256),
                      0, s, part, pl.splits, (int)a.M, (int)a.N, bias, a.Y, a.ldy);
   return hipGetLastError();
@@ -257,7 +258,6 @@ hipError_t launch_gemv(const GemvArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8) return hipErrorInvalidValue;
   const GvPlan pl = gv_plan(a.K, a.N);
-  if (pl.krange > GV_MAX_KR) return hipErrorInvalidValue;
   if (pl.splits > 1 && (a.ws == nullptr || a.ws_bytes < gemv_workspace(a.K, a.N)))
     return hipErrorInvalidValue;
   switch (a.epi) {

@@ -13,15 +13,19 @@ typedef short i16x4_t __attribute__((ext_vector_type(4)));
 // lds + 16*i.  Issued as inline assembly on purpose: the compiler then does
 // not count it as a pending LDS write, so it neither drains it at every
 // barrier nor before every ds_read; callers order it explicitly with
-// wait_vmcnt + barrier.
+// wait_vmcnt + barrier.  The compiler does not insert hazard wait states
+// into inline assembly, so the s_nop 4 supplies them: five wait states
+// cover both a VALU write of an SGPR operand (e.g. v_readfirstlane of the
+// base) and the M0 write that a vector-memory read of it must not follow
+// directly.
 __device__ __forceinline__ void dma16(const uint16_t *g, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(lds) : "memory");
 }
 
 // Same with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
 // offset: the per-block address arithmetic stays on the scalar unit.
 __device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_t lds) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
 // LDS byte address of a __shared__ pointer (wave-uniform).
