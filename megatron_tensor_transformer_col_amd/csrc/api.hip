@@ -203,7 +203,7 @@ int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni, con
   if (M == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  if (act != TP_ACT_SWIGLU && use_gemv(dtype, M) && Ni <= gemv_max_n()) {
+  if (act != TP_ACT_SWIGLU && use_gemv(dtype, M) && Ni <= gemv_max_n() && gemv_fits(ldx, ldw)) {
     const size_t need = gemv_workspace(K, Ni);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
       return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);
@@ -251,7 +251,7 @@ int tp_row_linear_partial(int dtype, int64_t M, int64_t Ki, int64_t N, const voi
   if (M == 0) return ok();
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  if (use_gemv(dtype, M) && N <= gemv_max_n()) {
+  if (use_gemv(dtype, M) && N <= gemv_max_n() && gemv_fits(ldx, ldw)) {
     const size_t need = gemv_workspace(Ki, N);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
       return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);

@@ -42,6 +42,7 @@ static constexpr int GV_WSLAB = GV_SLAB * GV_BN;  // W elements per stage (8 KiB
 static constexpr int GV_XSLAB = 16 * GV_SLAB;     // x elements per stage (2 KiB)
 static constexpr int GV_STAGE = GV_WSLAB + GV_XSLAB;
 static constexpr int GV_DMA = 3;                  // DMA ops per wave per stage (2 W + 1 x)
+static constexpr int64_t GV_MAX_LD = int64_t(1) << 26;  // 16 rows of either operand within 32-bit byte offsets
 
 struct GvPlan {
   int strips, splits, krange;
@@ -98,31 +99,42 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   //      (i%8) ^ swz(row), clamped into the matrix.  x: wave w fetches token
   //      rows 4w .. 4w+3 (lanes 0..31), granule (i%8) ^ (row & 7), token rows
   //      past M clamped to M-1.
-  int col_of[2];
+  // Byte offsets below are 32-bit (launch_gemv checks the strides), added to
+  // wave-uniform bases that the scalar unit computes per slab.
+  uint32_t woff[2];  // this lane's W source relative to its block's first row
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int row = (wave + 4 * j) * 8 + (lane >> 3);
     const int lg = (lane & 7) ^ gv_swz(row);
-    col_of[j] = min(n0 + lg * 8, N - 8);
+    const int colrel = min(n0 + lg * 8, N - 8) - n0;
+    woff[j] = (uint32_t)(((int64_t)(lane >> 3) * ldw + colrel) * 2);
   }
   const int xrow = 4 * wave + ((lane >> 3) & 3);
-  const uint16_t *xrow_ptr = X + (int64_t)min(xrow, M - 1) * ldx;
-  const int xgran = ((lane & 7) ^ (xrow & 7)) * 8;
+  const uint32_t xoff_row = (uint32_t)((int64_t)min(xrow, M - 1) * ldx * 2);
+  const uint32_t xoff = xoff_row + (uint32_t)(((lane & 7) ^ (xrow & 7)) * 16);
+  const uint16_t *Wn = W + n0;
   const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int s) {
     const int kr = k_begin + s * GV_SLAB;
     const uint32_t base = lds0 + (uint32_t)((s % GV_STAGES) * GV_STAGE * 2);
+    if (s != tail) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      // rows past K are clamped to K-1: valid memory, matched by zero x
-      const int row = min(kr + (wave + 4 * j) * 8 + (lane >> 3), K - 1);
-      dma16(W + (int64_t)row * ldw + col_of[j], base + (wave + 4 * j) * 1024);
+      for (int j = 0; j < 2; ++j)
+        dma16s(woff[j], Wn + (int64_t)(kr + (wave + 4 * j) * 8) * ldw, base + (wave + 4 * j) * 1024);
+      if (lane < 32) dma16s(xoff, X + kr, base + GV_WSLAB * 2 + wave * 512);
+    } else {
+      // rows past K are clamped to K-1 (valid memory, matched by zero x in
+      // xtail); the x DMA re-reads the first 8 elements of the row (valid for
+      // any K) so every wave issues the same number of ops per stage
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rb = min(kr + (wave + 4 * j) * 8, K - 1);
+        const int r = min(kr + (wave + 4 * j) * 8 + (lane >> 3), K - 1) - rb;
+        const uint32_t off = woff[j] - (uint32_t)((int64_t)(lane >> 3) * ldw * 2) + (uint32_t)((int64_t)r * ldw * 2);
+        dma16s(off, Wn + (int64_t)rb * ldw, base + (wave + 4 * j) * 1024);
+      }
+      if (lane < 32) dma16s(xoff_row, X, base + GV_WSLAB * 2 + wave * 512);
     }
-    // the tail slab's x comes from xtail; its DMA re-reads the first 8
-    // elements of the row (valid for any K) so every wave issues the same
-    // number of ops per stage
-    const uint16_t *xs = (s == tail) ? xrow_ptr : xrow_ptr + kr + xgran;
-    if (lane < 32) dma16(xs, base + GV_WSLAB * 2 + wave * 512);
   };
 
   // ---- prologue: STAGES-1 slabs in flight, then the zero-padded tail of x
@@ -192,42 +204,33 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   }
 }
 
-// Y[m][c..c+3] = epi(sum_s part[s][m][c..c+3] + bias), splits added in order.
+// Y[m][c] = epi(sum_s part[s][m][c] + bias), splits added in order.  One
+// thread per output element, all of its (at most 16 per batch) partial loads
+// issued before the first add, so the kernel costs about one memory latency.
 template <int EPI>
 __global__ void __launch_bounds__(256)
 gemv_finalize_kernel(const float *__restrict__ part, int splits, int M, int N,
                      const uint16_t *bias, void *Y, int64_t ldy) {
-  const int n4 = N / 4;
   const int v = blockIdx.x * 256 + threadIdx.x;
-  if (v >= M * n4) return;
-  const int m = v / n4, col = (v % n4) * 4;
+  if (v >= M * N) return;
+  const int m = v / N, col = v % N;
   const float *p = part + (int64_t)m * N + col;
   const int64_t step = (int64_t)16 * N;
-  f32x4_t s = *reinterpret_cast<const f32x4_t *>(p);
-  int sp = 1;
-  for (; sp + 4 <= splits; sp += 4) {  // four loads in flight, added in split order
-    const f32x4_t a = *reinterpret_cast<const f32x4_t *>(p + sp * step);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t *>(p + (sp + 1) * step);
-    const f32x4_t c = *reinterpret_cast<const f32x4_t *>(p + (sp + 2) * step);
-    const f32x4_t d = *reinterpret_cast<const f32x4_t *>(p + (sp + 3) * step);
-    s += a; s += b; s += c; s += d;
-  }
-  for (; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t *>(p + sp * step);
-  float r[4] = {s[0], s[1], s[2], s[3]};
-  if (bias != nullptr) {
-    const uint2 b = *reinterpret_cast<const uint2 *>(bias + col);
-    r[0] += bf2f((uint16_t)(b.x & 0xffffu)); r[1] += bf2f((uint16_t)(b.x >> 16));
-    r[2] += bf2f((uint16_t)(b.y & 0xffffu)); r[3] += bf2f((uint16_t)(b.y >> 16));
-  }
-  if constexpr (EPI == EPI_STORE_F32) {
-    *reinterpret_cast<float4 *>(static_cast<float *>(Y) + (int64_t)m * ldy + col) = make_float4(r[0], r[1], r[2], r[3]);
-  } else {
-    if constexpr (EPI == EPI_GELU) {
+  float sum = 0.f;
+  for (int s0 = 0; s0 < splits; s0 += 16) {
+    float t[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] = gelu_f(r[j]);
-    }
-    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + (int64_t)m * ldy + col) =
-        make_uint2(pack_bf2(r[0], r[1]), pack_bf2(r[2], r[3]));
+    for (int j = 0; j < 16; ++j) t[j] = (s0 + j < splits) ? p[(int64_t)(s0 + j) * step] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (s0 + j < splits) sum += t[j];
+  }
+  if (bias != nullptr) sum += bf2f(bias[col]);
+  if constexpr (EPI == EPI_STORE_F32) {
+    static_cast<float *>(Y)[(int64_t)m * ldy + col] = sum;
+  } else {
+    if constexpr (EPI == EPI_GELU) sum = gelu_f(sum);
+    static_cast<uint16_t *>(Y)[(int64_t)m * ldy + col] = f2bf(sum);
   }
 }
 
@@ -248,15 +251,18 @@ static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
                      (int)a.M, W, a.ldw, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int total = (int)a.M * (int)(a.N / 4);
+  const int total = (int)a.M * (int)a.N;
   hipLaunchKernelGGL((gemv_finalize_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256),
                      0, s, part, pl.splits, (int)a.M, (int)a.N, bias, a.Y, a.ldy);
   return hipGetLastError();
 }
 
+bool gemv_fits(int64_t ldx, int64_t ldw) { return ldx <= GV_MAX_LD && ldw <= GV_MAX_LD; }
+
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8) return hipErrorInvalidValue;
+  if (!gemv_fits(a.ldx, a.ldw)) return hipErrorInvalidValue;
   const GvPlan pl = gv_plan(a.K, a.N);
   if (pl.splits > 1 && (a.ws == nullptr || a.ws_bytes < gemv_workspace(a.K, a.N)))
     return hipErrorInvalidValue;

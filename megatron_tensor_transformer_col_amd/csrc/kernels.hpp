@@ -56,6 +56,7 @@ struct GemvArgs {
 };
 size_t gemv_workspace(int64_t K, int64_t N);
 int64_t gemv_max_n();  // widest N the split-K decode path accepts
+bool gemv_fits(int64_t ldx, int64_t ldw);  // row strides the decode path's 32-bit offsets cover
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
 
 // Y = sum_i P_i (+ bias), float32 partials, float32 or bf16 output.
