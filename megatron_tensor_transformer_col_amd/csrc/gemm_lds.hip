@@ -36,11 +36,16 @@
 
 namespace tpcol {
 
-// k-contiguous rows of BK elements (BK/8 granules); granule swizzle per row
+// k-contiguous rows of BK elements (BK/8 granules); granule swizzle per row.
+// For 32-deep slabs (64-byte rows) the fragment read (16 consecutive rows,
+// one granule each, per 16-lane group) is free of bank conflicts on gfx950
+// with granule c of row r stored at c ^ ((r >> 1) & 3), as measured with the
+// LDS bank-conflict counter; XOR patterns that also mix in row bit 3 cost
+// four conflict cycles per read.
 template <int BK>
 __device__ __forceinline__ int swz_k(int r) {
   if constexpr (BK == 64) return (r & 7) ^ ((r >> 3) & 1);
-  else return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r >> 1) & 3;
 }
 __device__ __forceinline__ int swz_mn(int r) { return ((r & 3) | (((r >> 3) & 1) << 2)) << 1; }
 
