@@ -206,3 +206,31 @@ def mha(X, Wq, Wk, Wv, Wo, heads, b, s, causal=True):
             c = slice(t * d, (t + 1) * d)
             O[r, c] = attention_heads(Q[r, c], K[r, c], V[r, c], causal)
     return {"Q": Q, "K": K, "V": V, "O": O, "Y": O @ Wo}
+
+
+def mha_gqa(X, Wq, Wk, Wv, Wo, heads, kv_heads, b, s, causal=True):
+    """Unsharded grouped-query attention block ("张量并行", 相关分析: GQA has
+    num_attention_heads query heads but only num_kv_heads key/value heads,
+    heads >= kv_heads).  Query head t reads key/value head t // g with
+    g = heads / kv_heads, the grouping of consecutive query heads; with
+    kv_heads == heads this is ``mha``.
+
+    Wq, Wo: [h, h] (d = h / heads); Wk, Wv: [h, kv_heads * d], kv head u in
+    columns u*d .. (u+1)*d - 1.  Returns Q, K, V, O (token-major) and Y."""
+    X, Wq, Wk, Wv, Wo = _f64(X), _f64(Wq), _f64(Wk), _f64(Wv), _f64(Wo)
+    h = X.shape[1]
+    if h % heads or heads % kv_heads:
+        raise ValueError("heads must divide h and be a multiple of kv_heads")
+    d = h // heads
+    g = heads // kv_heads
+    if Wk.shape[1] != kv_heads * d or Wv.shape[1] != kv_heads * d:
+        raise ValueError("Wk / Wv must have kv_heads * d columns")
+    Q, K, V = X @ Wq, X @ Wk, X @ Wv
+    O = np.zeros((b * s, heads * d), dtype=np.float64)
+    for bi in range(b):
+        r = slice(bi * s, (bi + 1) * s)
+        for t in range(heads):
+            u = t // g
+            cq, ckv = slice(t * d, (t + 1) * d), slice(u * d, (u + 1) * d)
+            O[r, cq] = attention_heads(Q[r, cq], K[r, ckv], V[r, ckv], causal)
+    return {"Q": Q, "K": K, "V": V, "O": O, "Y": O @ Wo}

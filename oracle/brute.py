@@ -131,3 +131,25 @@ def mha(X, Wq, Wk, Wv, Wo, heads, b, s, causal=True):
             for i in range(s):
                 O[bi * s + i][t * d:(t + 1) * d] = Ot[i]
     return {"O": O, "Y": matmul(O, Wo)}
+
+
+def mha_gqa(X, Wq, Wk, Wv, Wo, heads, kv_heads, b, s, causal=True):
+    """Grouped-query attention by loops: query head t attends with key/value
+    head t // (heads // kv_heads)."""
+    X = _rows(X)
+    h = len(X[0])
+    d = h // heads
+    g = heads // kv_heads
+    Q, K, V = matmul(X, Wq), matmul(X, Wk), matmul(X, Wv)
+    O = [[0.0] * (heads * d) for _ in range(b * s)]
+    for bi in range(b):
+        for t in range(heads):
+            u = t // g
+            rows = range(bi * s, (bi + 1) * s)
+            Qt = [Q[r][t * d:(t + 1) * d] for r in rows]
+            Kt = [K[r][u * d:(u + 1) * d] for r in rows]
+            Vt = [V[r][u * d:(u + 1) * d] for r in rows]
+            Ot = attention_head(Qt, Kt, Vt, causal)
+            for i in range(s):
+                O[bi * s + i][t * d:(t + 1) * d] = Ot[i]
+    return {"O": O, "Y": matmul(O, Wo)}

@@ -27,7 +27,8 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "round_to_bf16_bits", "bf16_bits_to_f32",
     "Tensor", "draw_normal", "make_mlp_inputs", "make_swiglu_inputs",
-    "make_mha_inputs", "column_shard", "row_shard", "qkv_shard", "out_shard",
+    "make_mha_inputs", "make_gqa_inputs", "column_shard", "row_shard", "qkv_shard",
+    "gqa_qkv_shard", "gqa_kv_heads_of_shard", "out_shard",
 ]
 
 
@@ -44,6 +45,7 @@ class Workload:
     h: int
     ffn: int = 0
     heads: int = 0
+    kv_heads: int = 0    # grouped-query attention: key/value heads (0: = heads)
     n_shards: int = 1
     causal: bool = True
     backward: bool = False
@@ -80,6 +82,10 @@ WORKLOADS: Dict[str, Workload] = {
     # head-sharded causal MHA, 32 heads of 128, 8 heads per shard
     "mha_heads_bf16": Workload("mha_heads_bf16", "mha", "bf16", b=4, s=2048, h=4096,
                                heads=32, n_shards=4, causal=True),
+    # grouped-query attention shard (Llama-3-8B-like 32 query / 8 key-value
+    # heads of 128), 8 query heads and their 2 key/value heads per shard
+    "gqa_heads_bf16": Workload("gqa_heads_bf16", "gqa", "bf16", b=4, s=2048, h=4096,
+                               heads=32, kv_heads=8, n_shards=4, causal=True),
     # decode-phase MLP shard: 16 single-token requests, memory-bound GEMV
     "decode_mlp_bf16": Workload("decode_mlp_bf16", "decode_gelu", "bf16", b=16, s=1,
                                 h=8192, ffn=28672, n_shards=8),
@@ -200,6 +206,17 @@ def make_mha_inputs(T: int, h: int, dtype: str, seed: int = 0, w_std: float = 0.
     return d
 
 
+def make_gqa_inputs(T: int, h: int, heads: int, kv_heads: int, dtype: str, seed: int = 0,
+                    w_std: float = 0.02, row_block: int = 1 << 30):
+    """X[T,h], Wq [h,h], Wk, Wv [h, kv_heads*d], Wo [h,h] (d = h / heads)."""
+    d = h // heads
+    rng = np.random.default_rng(seed)
+    out = {"X": draw_normal(rng, (T, h), 1.0, dtype, row_block)}
+    for name, cols in (("Wq", h), ("Wk", kv_heads * d), ("Wv", kv_heads * d), ("Wo", h)):
+        out[name] = draw_normal(rng, (h, cols), w_std, dtype, row_block)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # Shard slicing (index bookkeeping only): contiguous blocks in index order
 # ---------------------------------------------------------------------------
@@ -230,3 +247,35 @@ def qkv_shard(Wq: Tensor, Wk: Tensor, Wv: Tensor, i: int, n: int, heads: int) ->
 
 def out_shard(Wo: Tensor, i: int, n: int) -> Tensor:
     return row_shard(Wo, i, n)
+
+
+def gqa_kv_heads_of_shard(i: int, n: int, heads: int, kv_heads: int):
+    """Global key/value heads that shard i's query heads i*heads/n ..
+    (i+1)*heads/n - 1 read (query head t reads kv head t // (heads/kv_heads)):
+    kv_heads/n of them when n <= kv_heads, else the one kv head of the group,
+    replicated on n/kv_heads shards."""
+    hl, g = heads // n, heads // kv_heads
+    first, last = (i * hl) // g, (i * hl + hl - 1) // g
+    return list(range(first, last + 1))
+
+
+def gqa_qkv_shard(Wq: Tensor, Wk: Tensor, Wv: Tensor, i: int, n: int, heads: int,
+                  kv_heads: int) -> Tensor:
+    """Packed [Wq_i | Wk_i | Wv_i] of a grouped-query shard: the shard's
+    heads/n query heads, then the key and value columns of the kv heads they
+    read (``gqa_kv_heads_of_shard``)."""
+    if heads % n or heads % kv_heads:
+        raise ValueError("heads must be a multiple of the shard count and of kv_heads")
+    if n > kv_heads and n % kv_heads:
+        raise ValueError("with more shards than kv heads, kv_heads must divide the shard count")
+    d = Wq.shape[1] // heads
+    kv = gqa_kv_heads_of_shard(i, n, heads, kv_heads)
+    q = column_shard(Wq, i, n)
+    ks = [Wk.slice_cols(u * d, (u + 1) * d) for u in kv]
+    vs = [Wv.slice_cols(u * d, (u + 1) * d) for u in kv]
+    parts = [q] + ks + vs
+    f32 = np.ascontiguousarray(np.concatenate([p.f32 for p in parts], axis=1))
+    bits = None
+    if Wq.bits is not None:
+        bits = np.ascontiguousarray(np.concatenate([p.bits for p in parts], axis=1))
+    return Tensor(f32, Wq.dtype, bits)
