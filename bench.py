@@ -18,7 +18,8 @@ the timed steps.  The JSON line also carries: the roofline of the dominant
 kernel (the column GEMM + GELU, timed with HIP events over back-to-back
 launches on the launch stream), the fp64 CPU oracle timed on this host as a
 baseline, and per-row figures for the other workloads (SwiGLU forward /
-backward, head-sharded attention, decode GEMV) unless --no-rows.
+backward, head-sharded and grouped-query attention, decode GEMV) unless
+--no-rows.
 """
 import argparse
 import json
@@ -243,6 +244,26 @@ class Rows:
         self.tp.tp_attn_heads_shard(s["X"], s["Wqkv"], s["Wo"], s["P"], b, sq, hl, dh, causal=True,
                                     ws=s["ws"])
 
+    # ---- grouped-query attention shard: b 4, s 2048, h 4096, 32 query / 8
+    #      kv heads of 128 over 4 shards -> 8 query + 2 kv heads per shard
+    def gqa(self):
+        t = self.torch
+        b, sq, h, hl, kvl, dh = 4, 2048, 4096, 8, 2, 128
+        T = b * sq
+        s = {"X": self.randn((T, h), 1.0), "Wqkv": self.randn((h, (hl + 2 * kvl) * dh), 0.02),
+             "Wo": self.randn((hl * dh, h), 0.02), "P": self.empty((T, h), t.float32),
+             "dims": (b, sq, hl, kvl, dh)}
+        s["ws"] = self.empty((self.tp.tp_attn_gqa_shard_workspace(1, b, sq, hl, kvl, dh),), t.uint8)
+        s["flop_qkv"] = 2.0 * T * h * (hl + 2 * kvl) * dh
+        s["flop_att"] = 4.0 * dh * (sq * (sq + 1) / 2) * b * hl
+        s["flop_o"] = 2.0 * T * hl * dh * h
+        return s
+
+    def gqa_attn(self, s):
+        b, sq, hl, kvl, dh = s["dims"]
+        self.tp.tp_attn_gqa_shard(s["X"], s["Wqkv"], s["Wo"], s["P"], b, sq, hl, kvl, dh, causal=True,
+                                  ws=s["ws"])
+
     # ---- decode GEMV: 16 tokens, h 8192, ffn 28672 / 8, all 8 shards
     #      (940 MB of weights > the 256 MB Infinity Cache: every GEMV streams from HBM)
     def decode(self):
@@ -290,6 +311,14 @@ def rows(torch, tp, steps, warmup):
                               "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
                               "note": "QKV GEMM + causal attention (4*d*s(s+1)/2 per head) + W_o GEMM"}
     del s
+    s = R.gqa()
+    gq = graph_of(torch, lambda: R.gqa_attn(s))
+    ms_q, _ = timed(torch, lambda kt: gq.replay(), s_ms, w_ms)
+    fq = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
+    out["gqa_heads_shard"] = {"ms": ms_q, "tflops": fq / ms_q / 1e9,
+                              "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
+                              "note": "8 query + 2 kv heads: QKV GEMM + causal attention + W_o GEMM"}
+    del s
     s = R.decode()
     gd = graph_of(torch, lambda: R.decode_step(s))
     ms_d, _ = timed(torch, lambda kt: gd.replay(), s_ms, 3)
@@ -324,6 +353,9 @@ def run_op(torch, tp, synth, name, iters):
         elif name == "c4_attn":
             s = R.mha()
             fn = lambda: R.attn(s)
+        elif name == "c6_gqa":
+            s = R.gqa()
+            fn = lambda: R.gqa_attn(s)
         elif name.startswith("c5_"):
             s = R.decode()
             k = {"c5_col": 0, "c5_row": 1}[name]

@@ -141,6 +141,33 @@ size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s,
                                      int64_t heads_local, int64_t d);
 
 /*
+ * Grouped-query variant of tp_attn_heads_shard: the shard holds heads_local
+ * query heads and kv_heads_local key/value heads; query head t (local) reads
+ * key/value head t / (heads_local / kv_heads_local), i.e. consecutive groups
+ * of query heads share one key/value head ("张量并行", 相关分析: GQA has
+ * num_attention_heads >= num_kv_heads, and K/V heads must stay consistent
+ * across shards).  With more shards than key/value heads, each shard holds
+ * the one key/value head its query heads read, replicated on the shards of
+ * the group.  kv_heads_local == heads_local is tp_attn_heads_shard.
+ *   Wqkv [h x (heads_local + 2*kv_heads_local)*d]: Q heads, then K heads,
+ *        then V heads, head u at offset u*d inside its block.
+ *   ws   tp_attn_gqa_shard_workspace() bytes: QKV_i [b*s x (hl + 2*kvl)*d]
+ *        then O_i [b*s x hl*d], bf16 row-major, readable after the call.
+ * heads_local must be a multiple of kv_heads_local, and
+ * (heads_local + 2*kv_heads_local)*d at most 2^24 (TP_ERR_SHAPE); otherwise
+ * as tp_attn_heads_shard.
+ */
+int tp_attn_gqa_shard(int dtype, int64_t b, int64_t s, int64_t h,
+                      int64_t heads_local, int64_t kv_heads_local, int64_t d, int causal,
+                      const void *X, int64_t ldx,
+                      const void *Wqkv, int64_t ldwqkv,
+                      const void *Wo, int64_t ldwo,
+                      float *P, int64_t ldp,
+                      void *ws, size_t ws_bytes, void *stream);
+size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
+                                   int64_t kv_heads_local, int64_t d);
+
+/*
  * Sum of the N shard partials, added in shard order in float32, plus an
  * optional bias added once:
  *     Y = sum_{i<n} P_i (+ bias)

@@ -21,6 +21,7 @@ import threading
 __all__ = [
     "TpError", "lib", "library_path", "TP_F32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU_ERF",
     "TP_ACT_SWIGLU", "tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_heads_shard",
+    "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace",
     "tp_shard_sum", "tp_mlp_shard_backward", "tp_check_split", "tp_set_gemv_max_m",
     "tp_status_string", "tp_last_error", "tp_col_linear_gelu_workspace",
     "tp_row_linear_partial_workspace", "tp_attn_heads_shard_workspace",
@@ -44,6 +45,9 @@ _SIGS = {
     "tp_attn_heads_shard": (_int, [_int, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp,
                                    _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "tp_attn_heads_shard_workspace": (_sz, [_int, _i64, _i64, _i64, _i64]),
+    "tp_attn_gqa_shard": (_int, [_int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp,
+                                 _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "tp_attn_gqa_shard_workspace": (_sz, [_int, _i64, _i64, _i64, _i64, _i64]),
     "tp_shard_sum": (_int, [_int, _i64, _i64, _int, ctypes.POINTER(_vp), _i64, _vp, _vp, _i64,
                             _vp]),
     "tp_mlp_shard_backward": (_int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
@@ -183,6 +187,10 @@ def tp_attn_heads_shard_workspace(dtype, b, s, heads_local, d) -> int:
     return lib().tp_attn_heads_shard_workspace(dtype, b, s, heads_local, d)
 
 
+def tp_attn_gqa_shard_workspace(dtype, b, s, heads_local, kv_heads_local, d) -> int:
+    return lib().tp_attn_gqa_shard_workspace(dtype, b, s, heads_local, kv_heads_local, d)
+
+
 def tp_mlp_shard_backward_workspace(dtype, act, M, Ni) -> int:
     return lib().tp_mlp_shard_backward_workspace(dtype, act, M, Ni)
 
@@ -229,6 +237,24 @@ def tp_attn_heads_shard(X, Wqkv, Wo, P, b, s, heads_local, d=128, causal=True, w
     _check("tp_attn_heads_shard", lib().tp_attn_heads_shard(
         dt, b, s, h, heads_local, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo, pp, ldp,
         pws, nws, _stream(stream, X)))
+    return P
+
+
+def tp_attn_gqa_shard(X, Wqkv, Wo, P, b, s, heads_local, kv_heads_local, d=128, causal=True,
+                      ws=None, stream=None):
+    """Grouped-query attention over this shard's query heads (each group of
+    heads_local / kv_heads_local consecutive query heads reads one of the
+    shard's kv heads), then the float32 partial P = O_i Wo_i."""
+    dt = _dtype_code(X)
+    px, _, h, ldx = _mat(X, "X")
+    pq, _, _, ldq = _mat(Wqkv, "Wqkv")
+    po, _, _, ldo = _mat(Wo, "Wo")
+    pp, _, _, ldp = _mat(P, "P")
+    need = tp_attn_gqa_shard_workspace(dt, b, s, heads_local, kv_heads_local, d)
+    pws, nws = _workspace(ws, need, X.device, zeroed=False)
+    _check("tp_attn_gqa_shard", lib().tp_attn_gqa_shard(
+        dt, b, s, h, heads_local, kv_heads_local, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo,
+        pp, ldp, pws, nws, _stream(stream, X)))
     return P
 
 

@@ -108,13 +108,72 @@ BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
 struct AttnWs {
   size_t qkv, o, total;
 };
-AttnWs attn_ws(int64_t b, int64_t s, int64_t hl, int64_t d) {
+AttnWs attn_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
   const size_t T = (size_t)b * (size_t)s;
   AttnWs w;
   w.qkv = 0;
-  w.o = round256(T * 3 * (size_t)hl * (size_t)d * 2);
+  w.o = round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
   w.total = w.o + round256(T * (size_t)hl * (size_t)d * 2);
   return w;
+}
+
+}  // namespace
+
+namespace {
+int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
+                     int64_t kv_heads_local, int64_t d, int causal, const void *X, int64_t ldx,
+                     const void *Wqkv, int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P,
+                     int64_t ldp, void *ws, size_t ws_bytes, void *stream) {
+  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports bf16 only");
+  TRY(check_dims({b, s_len, h, heads_local, kv_heads_local, d}, fn));
+  if (h < 1 || heads_local < 1) return fail(TP_ERR_SHAPE, "h and heads_local must be >= 1");
+  if (kv_heads_local < 1 || heads_local % kv_heads_local)
+    return fail(TP_ERR_SHAPE, "heads_local %lld is not a multiple of kv_heads_local %lld",
+                (long long)heads_local, (long long)kv_heads_local);
+  if (d != 128) return fail(TP_ERR_SHAPE, "head dim %lld unsupported (128 only)", (long long)d);
+  const int64_t T = b * s_len;
+  if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
+  const int64_t w = heads_local * d;
+  const int64_t wqkv = (heads_local + 2 * kv_heads_local) * d;
+  if (wqkv > (int64_t(1) << 24))
+    return fail(TP_ERR_SHAPE, "(heads_local + 2*kv_heads_local)*d must be <= 2^24");
+  TRY(check_mat(X, T, h, ldx, 2, "X"));
+  TRY(check_mat(Wqkv, h, wqkv, ldwqkv, 2, "Wqkv"));
+  TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));
+  TRY(check_mat(P, T, h, ldp, 4, "P"));
+  if (T == 0) return ok();
+  const AttnWs L = attn_ws(b, s_len, heads_local, kv_heads_local, d);
+  if (ws == nullptr || ws_bytes < L.total)
+    return fail(TP_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", L.total, ws_bytes);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char *base = static_cast<char *>(ws);
+  void *qkv = base + L.qkv;
+  void *O = base + L.o;
+
+  GemmArgs q;
+  q.dtype = DT_BF16;
+  q.layout = LAY_NN;
+  q.epi = EPI_STORE;
+  q.M = T; q.N = wqkv; q.K = h;
+  q.A = X; q.lda = ldx;
+  q.B = Wqkv; q.ldb = ldwqkv;
+  q.C = qkv; q.ldc = wqkv;
+  TRY(hip_status(launch_gemm(q, st), "QKV GEMM"));
+  TRY(hip_status(launch_flash_attn(qkv, wqkv, O, w, b, s_len, heads_local, kv_heads_local, d,
+                                   causal != 0, st),
+                 "attention"));
+  GemmArgs o;
+  o.dtype = DT_BF16;
+  o.layout = LAY_NN;
+  o.epi = EPI_STORE_F32;
+  o.M = T; o.N = h; o.K = w;
+  o.A = O; o.lda = w;
+  o.B = Wo; o.ldb = ldwo;
+  o.C = P; o.ldc = ldp;
+  TRY(hip_status(launch_gemm(o, st), "output GEMM"));
+  return ok();
 }
 
 }  // namespace
@@ -171,7 +230,14 @@ size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s, int64_t he
                                      int64_t d) {
   (void)dtype;
   if (b < 0 || s < 0 || heads_local < 0 || d < 0) return 0;
-  return attn_ws(b, s, heads_local, d).total;
+  return attn_ws(b, s, heads_local, heads_local, d).total;
+}
+
+size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
+                                   int64_t kv_heads_local, int64_t d) {
+  (void)dtype;
+  if (b < 0 || s < 0 || heads_local < 0 || kv_heads_local < 0 || d < 0) return 0;
+  return attn_ws(b, s, heads_local, kv_heads_local, d).total;
 }
 
 size_t tp_mlp_shard_backward_workspace(int dtype, int act, int64_t M, int64_t Ni) {
@@ -282,52 +348,16 @@ int tp_attn_heads_shard(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t 
                         int64_t d, int causal, const void *X, int64_t ldx, const void *Wqkv,
                         int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P, int64_t ldp,
                         void *ws, size_t ws_bytes, void *stream) {
-  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports bf16 only");
-  TRY(check_dims({b, s_len, h, heads_local, d}, "tp_attn_heads_shard"));
-  if (h < 1 || heads_local < 1) return fail(TP_ERR_SHAPE, "h and heads_local must be >= 1");
-  if (d != 128) return fail(TP_ERR_SHAPE, "head dim %lld unsupported (128 only)", (long long)d);
-  const int64_t T = b * s_len;
-  if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
-  const int64_t w = heads_local * d;
-  if (3 * w > (int64_t(1) << 24))
-    return fail(TP_ERR_SHAPE, "heads_local %lld too large (3*heads_local*d must be <= 2^24)",
-                (long long)heads_local);
-  TRY(check_mat(X, T, h, ldx, 2, "X"));
-  TRY(check_mat(Wqkv, h, 3 * w, ldwqkv, 2, "Wqkv"));
-  TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));
-  TRY(check_mat(P, T, h, ldp, 4, "P"));
-  if (T == 0) return ok();
-  const AttnWs L = attn_ws(b, s_len, heads_local, d);
-  if (ws == nullptr || ws_bytes < L.total)
-    return fail(TP_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", L.total, ws_bytes);
-  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
-    return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char *base = static_cast<char *>(ws);
-  void *qkv = base + L.qkv;
-  void *O = base + L.o;
+  return attn_impl("tp_attn_heads_shard", dtype, b, s_len, h, heads_local, heads_local, d, causal, X,
+                   ldx, Wqkv, ldwqkv, Wo, ldwo, P, ldp, ws, ws_bytes, stream);
+}
 
-  GemmArgs q;
-  q.dtype = DT_BF16;
-  q.layout = LAY_NN;
-  q.epi = EPI_STORE;
-  q.M = T; q.N = 3 * w; q.K = h;
-  q.A = X; q.lda = ldx;
-  q.B = Wqkv; q.ldb = ldwqkv;
-  q.C = qkv; q.ldc = 3 * w;
-  TRY(hip_status(launch_gemm(q, st), "QKV GEMM"));
-  TRY(hip_status(launch_flash_attn(qkv, 3 * w, O, w, b, s_len, heads_local, d, causal != 0, st),
-                 "attention"));
-  GemmArgs o;
-  o.dtype = DT_BF16;
-  o.layout = LAY_NN;
-  o.epi = EPI_STORE_F32;
-  o.M = T; o.N = h; o.K = w;
-  o.A = O; o.lda = w;
-  o.B = Wo; o.ldb = ldwo;
-  o.C = P; o.ldc = ldp;
-  TRY(hip_status(launch_gemm(o, st), "output GEMM"));
-  return ok();
+int tp_attn_gqa_shard(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
+                      int64_t kv_heads_local, int64_t d, int causal, const void *X, int64_t ldx,
+                      const void *Wqkv, int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P,
+                      int64_t ldp, void *ws, size_t ws_bytes, void *stream) {
+  return attn_impl("tp_attn_gqa_shard", dtype, b, s_len, h, heads_local, kv_heads_local, d, causal, X,
+                   ldx, Wqkv, ldwqkv, Wo, ldwo, P, ldp, ws, ws_bytes, stream);
 }
 
 int tp_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *partials,

@@ -1,4 +1,7 @@
 // Head-local attention for one tensor-parallel shard (bf16, head dim 128).
+// Multi-head, or grouped-query with kv_heads_local key/value heads shared by
+// consecutive groups of heads_local / kv_heads_local query heads
+// ("张量并行", 相关分析: GQA).
 //
 // Each shard owns heads_local whole heads, so attention needs nothing from
 // other shards ("张量并行", Multi-Head Attention 的并行化: heads are
@@ -87,6 +90,7 @@ struct FaArgs {
   uint16_t *O;
   int64_t ldo;
   int s, hl, nqb, items;  // items: workgroups per (sequence, head)
+  int kvl, group;         // key/value heads in the shard; query heads per kv head
   float scale_log2;       // log2(e) / sqrt(d)
 };
 
@@ -175,8 +179,9 @@ struct FaBlock {
   __device__ __forceinline__ void run(const FaArgs &a, int bi, int head, int qb) const {
     const int64_t tok0 = (int64_t)bi * a.s;
     const uint16_t *Qg = a.qkv + tok0 * a.ldq + head * FA_D;
-    const uint16_t *Kg = a.qkv + tok0 * a.ldq + (a.hl + head) * FA_D;
-    const uint16_t *Vg = a.qkv + tok0 * a.ldq + (2 * a.hl + head) * FA_D;
+    const int kvh = head / a.group;  // grouped-query: the kv head this query head reads
+    const uint16_t *Kg = a.qkv + tok0 * a.ldq + (a.hl + kvh) * FA_D;
+    const uint16_t *Vg = a.qkv + tok0 * a.ldq + (a.hl + a.kvl + kvh) * FA_D;
     const int q0 = qb * FA_BQ;
     const int q_w = q0 + wq * FA_QW;
 
@@ -364,7 +369,8 @@ __global__ void __launch_bounds__(FA_NW * 64) flash_attn_kernel(FaArgs a) {
   fb.lds0 = lds_addr(smem);
 
   // workgroup -> (sequence, head, item); the 8 XCDs each get a contiguous
-  // run of (sequence, head) pairs so their K/V stay in that XCD's L2
+  // run of (sequence, head) pairs so their K/V stay in that XCD's L2 (query
+  // heads of one kv group are consecutive, so they share it too)
   const int nwg = (int)gridDim.x;
   int logical = (int)blockIdx.x;
   if ((nwg & 7) == 0) logical = (logical & 7) * (nwg >> 3) + (logical >> 3);
@@ -381,10 +387,11 @@ __global__ void __launch_bounds__(FA_NW * 64) flash_attn_kernel(FaArgs a) {
 }
 
 hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, int64_t b,
-                             int64_t s, int64_t heads_local, int64_t d, bool causal,
-                             hipStream_t st) {
+                             int64_t s, int64_t heads_local, int64_t kv_heads_local, int64_t d,
+                             bool causal, hipStream_t st) {
   if (b <= 0 || s <= 0 || heads_local <= 0) return hipSuccess;
   if (d != FA_D) return hipErrorInvalidValue;
+  if (kv_heads_local < 1 || heads_local % kv_heads_local) return hipErrorInvalidValue;
   if (ldqkv > FA_MAX_LD) return hipErrorInvalidValue;  // 32-bit DMA offsets
   FaArgs a;
   a.qkv = static_cast<const uint16_t *>(qkv);
@@ -393,6 +400,8 @@ hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ld
   a.ldo = ldo;
   a.s = (int)s;
   a.hl = (int)heads_local;
+  a.kvl = (int)kv_heads_local;
+  a.group = (int)(heads_local / kv_heads_local);
   a.nqb = (int)((s + FA_BQ - 1) / FA_BQ);
   a.items = causal ? (a.nqb + 1) / 2 : a.nqb;
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);

@@ -65,8 +65,8 @@ hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const fl
 
 // Head-local flash attention over a packed [Q|K|V] buffer (bf16, d = 128).
 hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, int64_t b,
-                             int64_t s, int64_t heads_local, int64_t d, bool causal,
-                             hipStream_t st);
+                             int64_t s, int64_t heads_local, int64_t kv_heads_local, int64_t d,
+                             bool causal, hipStream_t st);
 
 // db[n] = sum_m dZ[m][n] (dZ dtype, db float32).
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,

@@ -132,6 +132,23 @@ def test_attention_validation():
 
 
 @host_only
+def test_gqa_attention_validation():
+    lib = tp.lib()
+    g = lib.tp_attn_gqa_shard
+    # 8 query heads, 2 kv heads: Wqkv is (8 + 2*2)*128 = 1536 wide
+    assert g(1, 4, 2048, 4096, 8, 2, 128, 1, A, 4096, A, 1536, A, 4096, A, 4096, A, 1024, None) == -5
+    # heads_local not a multiple of kv_heads_local
+    assert g(1, 4, 2048, 4096, 8, 3, 128, 1, A, 4096, A, 1536, A, 4096, A, 4096, A, 1 << 30, None) == -2
+    assert g(1, 4, 2048, 4096, 8, 0, 128, 1, A, 4096, A, 1536, A, 4096, A, 4096, A, 1 << 30, None) == -2
+    # Wqkv narrower than (hl + 2 kvl) d
+    assert g(1, 4, 2048, 4096, 8, 2, 128, 1, A, 4096, A, 1024, A, 4096, A, 4096, A, 1 << 30, None) == -2
+    # workspace: QKV block (hl + 2 kvl) d wide, then O
+    T = 4 * 2048
+    assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 2, 128) == T * 1536 * 2 + T * 1024 * 2
+    assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 8, 128) == tp.tp_attn_heads_shard_workspace(1, 4, 2048, 8, 128)
+
+
+@host_only
 def test_shard_sum_and_backward_validation():
     lib = tp.lib()
     arr = (V * 3)(A, A, None)
