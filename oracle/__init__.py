@@ -29,5 +29,5 @@ from .block import (  # noqa: F401
     gelu, gelu_grad, silu, silu_grad, softmax_rows,
     linear, row_partial, shard_sum,
     mlp_gelu, mlp_swiglu, mlp_gelu_backward, mlp_swiglu_backward,
-    attention_heads, mha, mha_gqa,
+    attention_heads, mha, mha_gqa, layernorm, reduce_scatter_layernorm,
 )

@@ -234,3 +234,32 @@ def mha_gqa(X, Wq, Wk, Wv, Wo, heads, kv_heads, b, s, causal=True):
             cq, ckv = slice(t * d, (t + 1) * d), slice(u * d, (u + 1) * d)
             O[r, cq] = attention_heads(Q[r, cq], K[r, ckv], V[r, ckv], causal)
     return {"Q": Q, "K": K, "V": V, "O": O, "Y": O @ Wo}
+
+
+def layernorm(x, gamma, beta, eps):
+    """LN(x) = gamma * (x - mu(x)) / sqrt(sigma^2(x) + eps) + beta over the
+    last (hidden) dimension, mu and sigma^2 the mean and the population
+    variance of the full row ("张量并行", 相关分析: LayerNorm needs statistics
+    over the complete hidden dimension, so it cannot run on a column shard)."""
+    x = _f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return _f64(gamma) * (x - mu) / np.sqrt(var + eps) + _f64(beta)
+
+
+def reduce_scatter_layernorm(partials, gamma, beta, eps, n, rank, bias=None, residual=None):
+    """Sequence-parallel end of a tensor-parallel block (parallelism survey
+    post, 5 Sequence Parallelism: the all-reduce splits into reduce-scatter +
+    all-gather, and LayerNorm runs on each shard's 1/N of the tokens).
+
+    The full sum Ysum = sum_i P_i (+ bias once) (+ residual) of the shards'
+    partials, then rank's block of rows [rank*T/n, (rank+1)*T/n) of Ysum and
+    of LN(Ysum).  Returns {"Ysum": block, "Y": LN(block)}."""
+    full = shard_sum(partials, bias)
+    if residual is not None:
+        full = full + _f64(residual)
+    T = full.shape[0]
+    if T % n:
+        raise ValueError("token count must be a multiple of the shard count")
+    r = slice(rank * T // n, (rank + 1) * T // n)
+    return {"Ysum": full[r], "Y": layernorm(full[r], gamma, beta, eps)}

@@ -153,3 +153,15 @@ def mha_gqa(X, Wq, Wk, Wv, Wo, heads, kv_heads, b, s, causal=True):
             for i in range(s):
                 O[bi * s + i][t * d:(t + 1) * d] = Ot[i]
     return {"O": O, "Y": matmul(O, Wo)}
+
+
+def layernorm(x, gamma, beta, eps):
+    """Row by row: mean, population variance, normalise, scale and shift."""
+    out = []
+    for row in _rows(x):
+        n = len(row)
+        mu = sum(row) / n
+        var = sum((v - mu) ** 2 for v in row) / n
+        inv = 1.0 / math.sqrt(var + eps)
+        out.append([float(gamma[j]) * (row[j] - mu) * inv + float(beta[j]) for j in range(n)])
+    return out
