@@ -18,8 +18,8 @@ the timed steps.  The JSON line also carries: the roofline of the dominant
 kernel (the column GEMM + GELU, timed with HIP events over back-to-back
 launches on the launch stream), the fp64 CPU oracle timed on this host as a
 baseline, and per-row figures for the other workloads (SwiGLU forward /
-backward, head-sharded and grouped-query attention, decode GEMV) unless
---no-rows.
+backward, head-sharded and grouped-query attention, sequence-parallel
+reduce-scatter + LayerNorm, decode GEMV) unless --no-rows.
 """
 import argparse
 import json
@@ -264,6 +264,26 @@ class Rows:
         self.tp.tp_attn_gqa_shard(s["X"], s["Wqkv"], s["Wo"], s["P"], b, sq, hl, kvl, dh, causal=True,
                                   ws=s["ws"])
 
+    # ---- sequence-parallel reduce-scatter + LayerNorm, GPT-2-medium block end:
+    #      4 fp32 partials [8192 x 1024], bias, residual; 4 ranks x 2048 rows
+    def sp_ln(self):
+        t = self.torch
+        T, N, n = 8192, 1024, 4
+        f32 = lambda shape, std: t.randn(shape, generator=self.g, device="cuda:0", dtype=t.float32) * std
+        s = {"P": [f32((T, N), 1.0) for _ in range(n)], "bias": f32((N,), 0.1), "res": f32((T, N), 1.0),
+             "gamma": 1.0 + f32((N,), 0.1), "beta": f32((N,), 0.1), "n": n, "T": T,
+             "Ysum": self.empty((T, N), t.float32), "Y": self.empty((T, N), t.bfloat16)}
+        s["bytes"] = float(T) * N * (4 * n + 4 + 4 + 2)
+        return s
+
+    def sp_ln_step(self, s):
+        rows = s["T"] // s["n"]
+        for r in range(s["n"]):
+            sl = slice(r * rows, (r + 1) * rows)
+            self.tp.tp_shard_reduce_scatter_layernorm([p[sl] for p in s["P"]], s["gamma"], s["beta"], s["Y"][sl],
+                                                      eps=1e-5, bias=s["bias"], residual=s["res"][sl],
+                                                      Ysum=s["Ysum"][sl])
+
     # ---- decode GEMV: 16 tokens, h 8192, ffn 28672 / 8, all 8 shards
     #      (940 MB of weights > the 256 MB Infinity Cache: every GEMV streams from HBM)
     def decode(self):
@@ -319,6 +339,15 @@ def rows(torch, tp, steps, warmup):
                               "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
                               "note": "8 query + 2 kv heads: QKV GEMM + causal attention + W_o GEMM"}
     del s
+    s = R.sp_ln()
+    gl = graph_of(torch, lambda: R.sp_ln_step(s))
+    ms_l, _ = timed(torch, lambda kt: gl.replay(), s_ms, w_ms)
+    out["sp_reduce_scatter_layernorm"] = {"ms": ms_l, "bytes": s["bytes"], "gbs": s["bytes"] / ms_l / 1e6,
+                                          "frac_hbm_peak": s["bytes"] / ms_l / 1e6 / PEAK_HBM_GBS,
+                                          "note": "4 ranks x (sum of 4 fp32 partials + bias + residual, "
+                                                  "LayerNorm) per graph replay; bytes = partials + residual "
+                                                  "read, fp32 sum + bf16 output written"}
+    del s
     s = R.decode()
     gd = graph_of(torch, lambda: R.decode_step(s))
     ms_d, _ = timed(torch, lambda kt: gd.replay(), s_ms, 3)
@@ -356,6 +385,9 @@ def run_op(torch, tp, synth, name, iters):
         elif name == "c6_gqa":
             s = R.gqa()
             fn = lambda: R.gqa_attn(s)
+        elif name == "c7_spln":
+            s = R.sp_ln()
+            fn = lambda: R.sp_ln_step(s)
         elif name.startswith("c5_"):
             s = R.decode()
             k = {"c5_col": 0, "c5_row": 1}[name]

@@ -185,6 +185,37 @@ int tp_shard_sum(int out_dtype, int64_t M, int64_t N, int n,
                  const float *bias, void *Y, int64_t ldy, void *stream);
 
 /*
+ * Sequence-parallel end of a tensor-parallel block, for one rank: the
+ * all-reduce of the row-parallel partials splits into a reduce-scatter and
+ * an all-gather, and LayerNorm runs on the rank's reduce-scattered rows
+ * (parallelism survey post, 5 Sequence Parallelism).  For the `rows` token
+ * rows of this rank:
+ *     Ysum = sum_{i<n} P_i (+ bias, once) (+ residual)
+ *     Y    = gamma * (Ysum - mean) / sqrt(var + eps) + beta
+ * with mean and population variance over the full hidden row of N values
+ * ("张量并行", 相关分析: LayerNorm needs statistics of the complete hidden
+ * dimension).  Partials are added in shard order, then the bias, then the
+ * residual.  The caller passes each partial's pointer at the rank's first
+ * row (rank r of n holds token rows r*T/n .. (r+1)*T/n - 1 in the
+ * sequence-major token order); with Y pointing into one [T x N] buffer at
+ * the same row, the n ranks' outputs form the all-gathered activation.
+ *   partials  HOST array of n device pointers, each [rows x N] fp32, ldp
+ *   bias      [N] fp32 or NULL;  residual [rows x N] fp32 (ldr) or NULL
+ *   gamma, beta [N] fp32 (required);  eps >= 0
+ *   Ysum      [rows x N] fp32 (ldys) or NULL: the pre-norm sum (the
+ *             residual stream of the next block)
+ *   Y         [rows x N] out_dtype (ldy)
+ * N must be a multiple of 4 (fp32) / 8 (bf16 Y), 4 <= N <= 8192
+ * (TP_ERR_SHAPE); 1 <= n <= 64.
+ */
+int tp_shard_reduce_scatter_layernorm(int out_dtype, int64_t rows, int64_t N, int n,
+                                      const float *const *partials, int64_t ldp,
+                                      const float *bias, const float *residual, int64_t ldr,
+                                      const float *gamma, const float *beta, float eps,
+                                      float *Ysum, int64_t ldys,
+                                      void *Y, int64_t ldy, void *stream);
+
+/*
  * MLP shard backward given dY (broadcast to every shard):
  *   row layer    dW2_i = H_i^T dY,  dH_i = dY W2_i^T
  *   activation   dZ_i = dH_i * GELU'(Z_i)          (GELU; Z_i recomputed)

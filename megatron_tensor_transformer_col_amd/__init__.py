@@ -21,7 +21,7 @@ import threading
 __all__ = [
     "TpError", "lib", "library_path", "TP_F32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU_ERF",
     "TP_ACT_SWIGLU", "tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_heads_shard",
-    "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace",
+    "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace", "tp_shard_reduce_scatter_layernorm",
     "tp_shard_sum", "tp_mlp_shard_backward", "tp_check_split", "tp_set_gemv_max_m",
     "tp_status_string", "tp_last_error", "tp_col_linear_gelu_workspace",
     "tp_row_linear_partial_workspace", "tp_attn_heads_shard_workspace",
@@ -50,6 +50,9 @@ _SIGS = {
     "tp_attn_gqa_shard_workspace": (_sz, [_int, _i64, _i64, _i64, _i64, _i64]),
     "tp_shard_sum": (_int, [_int, _i64, _i64, _int, ctypes.POINTER(_vp), _i64, _vp, _vp, _i64,
                             _vp]),
+    "tp_shard_reduce_scatter_layernorm": (_int, [_int, _i64, _i64, _int, ctypes.POINTER(_vp), _i64, _vp,
+                                                 _vp, _i64, _vp, _vp, ctypes.c_float, _vp, _i64, _vp,
+                                                 _i64, _vp]),
     "tp_mlp_shard_backward": (_int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                      _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                      _i64, _vp, _sz, _vp]),
@@ -271,6 +274,30 @@ def tp_shard_sum(partials, Y, bias=None, stream=None):
     py, _, _, ldy = _mat(Y, "Y")
     _check("tp_shard_sum", lib().tp_shard_sum(
         _dtype_code(Y), M, N, n, arr, ldp, _ptr(bias), py, ldy, _stream(stream, Y)))
+    return Y
+
+
+def tp_shard_reduce_scatter_layernorm(partials, gamma, beta, Y, eps=1e-5, bias=None, residual=None,
+                                      Ysum=None, stream=None):
+    """This rank's rows of LN(sum_i partials[i] (+ bias) (+ residual)).
+
+    partials: float32 [rows x N] views at the rank's first row (e.g.
+    P[r*T//n:(r+1)*T//n]); Y: [rows x N] bf16 or float32; Ysum: optional
+    float32 [rows x N] for the pre-norm sum."""
+    n = len(partials)
+    if n == 0:
+        raise ValueError("need at least one partial")
+    _, rows, N, ldp = _mat(partials[0], "partials[0]")
+    for p in partials[1:]:
+        if tuple(p.shape) != (rows, N) or (rows > 1 and p.stride(0) != ldp):
+            raise ValueError("all partials must share shape and row stride")
+    arr = (ctypes.c_void_p * n)(*[p.data_ptr() for p in partials])
+    py, _, _, ldy = _mat(Y, "Y")
+    pr, _, _, ldr = _mat(residual, "residual")
+    ps, _, _, lds = _mat(Ysum, "Ysum")
+    _check("tp_shard_reduce_scatter_layernorm", lib().tp_shard_reduce_scatter_layernorm(
+        _dtype_code(Y), rows, N, n, arr, ldp, _ptr(bias), pr, ldr, _ptr(gamma), _ptr(beta), float(eps),
+        ps, lds, py, ldy, _stream(stream, Y)))
     return Y
 
 

@@ -381,6 +381,37 @@ int tp_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const 
   return ok();
 }
 
+int tp_shard_reduce_scatter_layernorm(int out_dtype, int64_t rows, int64_t N, int n,
+                                      const float *const *partials, int64_t ldp, const float *bias,
+                                      const float *residual, int64_t ldr, const float *gamma,
+                                      const float *beta, float eps, float *Ysum, int64_t ldys, void *Y,
+                                      int64_t ldy, void *stream) {
+  if (!dtype_ok(out_dtype)) return fail(TP_ERR_DTYPE, "dtype %d", out_dtype);
+  if (n < 1 || n > 64) return fail(TP_ERR_ARG, "shard count %d outside 1..64", n);
+  if (partials == nullptr) return fail(TP_ERR_ARG, "partials array is NULL");
+  if (gamma == nullptr || beta == nullptr) return fail(TP_ERR_ARG, "gamma and beta are required");
+  if (!(eps >= 0.0f)) return fail(TP_ERR_ARG, "eps must be >= 0");
+  TRY(check_dims({rows, N}, "tp_shard_reduce_scatter_layernorm"));
+  if (N < 4 || N > rs_layernorm_max_n())
+    return fail(TP_ERR_SHAPE, "hidden size %lld outside 4..%lld", (long long)N, (long long)rs_layernorm_max_n());
+  for (int i = 0; i < n; ++i) {
+    char name[32];
+    snprintf(name, sizeof(name), "partials[%d]", i);
+    TRY(check_mat(partials[i], rows, N, ldp, 4, name));
+  }
+  TRY(check_vec(bias, N, 4, "bias"));
+  TRY(check_vec(gamma, N, 4, "gamma"));
+  TRY(check_vec(beta, N, 4, "beta"));
+  if (residual != nullptr) TRY(check_mat(residual, rows, N, ldr, 4, "residual"));
+  if (Ysum != nullptr) TRY(check_mat(Ysum, rows, N, ldys, 4, "Ysum"));
+  TRY(check_mat(Y, rows, N, ldy, esize(out_dtype), "Y"));
+  if (rows == 0) return ok();
+  TRY(hip_status(launch_rs_layernorm(out_dtype, rows, N, n, partials, ldp, bias, residual, ldr, gamma, beta,
+                                     eps, Ysum, ldys, Y, ldy, static_cast<hipStream_t>(stream)),
+                 "reduce-scatter layernorm"));
+  return ok();
+}
+
 int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
                           int64_t ldx, const void *W1, int64_t ldw1, const void *Wup, int64_t ldwu,
                           const void *b1, const void *W2, int64_t ldw2, const void *dY,

@@ -69,6 +69,11 @@ hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ld
                              bool causal, hipStream_t st);
 
 // db[n] = sum_m dZ[m][n] (dZ dtype, db float32).
+hipError_t launch_rs_layernorm(int out_dtype, int64_t rows, int64_t N, int n, const float *const *parts,
+                               int64_t ldp, const float *bias, const float *res, int64_t ldr,
+                               const float *gamma, const float *beta, float eps, float *Ysum,
+                               int64_t ldys, void *Y, int64_t ldy, hipStream_t s);
+int64_t rs_layernorm_max_n();
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,
                          hipStream_t s);
 

@@ -28,7 +28,7 @@ __all__ = [
     "Workload", "WORKLOADS", "round_to_bf16_bits", "bf16_bits_to_f32",
     "Tensor", "draw_normal", "make_mlp_inputs", "make_swiglu_inputs",
     "make_mha_inputs", "make_gqa_inputs", "column_shard", "row_shard", "qkv_shard",
-    "gqa_qkv_shard", "gqa_kv_heads_of_shard", "out_shard",
+    "gqa_qkv_shard", "gqa_kv_heads_of_shard", "out_shard", "make_sp_inputs",
 ]
 
 
@@ -86,6 +86,11 @@ WORKLOADS: Dict[str, Workload] = {
     # heads of 128), 8 query heads and their 2 key/value heads per shard
     "gqa_heads_bf16": Workload("gqa_heads_bf16", "gqa", "bf16", b=4, s=2048, h=4096,
                                heads=32, kv_heads=8, n_shards=4, causal=True),
+    # sequence-parallel end of the GPT-2-medium-shaped block: 4 fp32 partials
+    # of [8192 x 1024] reduce-scattered over 4 ranks (2048 rows each), plus
+    # bias, residual and LayerNorm
+    "sp_ln_gpt2m": Workload("sp_ln_gpt2m", "sp_layernorm", "f32", b=8, s=1024, h=1024,
+                            n_shards=4),
     # decode-phase MLP shard: 16 single-token requests, memory-bound GEMV
     "decode_mlp_bf16": Workload("decode_mlp_bf16", "decode_gelu", "bf16", b=16, s=1,
                                 h=8192, ffn=28672, n_shards=8),
@@ -214,6 +219,19 @@ def make_gqa_inputs(T: int, h: int, heads: int, kv_heads: int, dtype: str, seed:
     out = {"X": draw_normal(rng, (T, h), 1.0, dtype, row_block)}
     for name, cols in (("Wq", h), ("Wk", kv_heads * d), ("Wv", kv_heads * d), ("Wo", h)):
         out[name] = draw_normal(rng, (h, cols), w_std, dtype, row_block)
+    return out
+
+
+def make_sp_inputs(T: int, N: int, n: int, seed: int = 0):
+    """n fp32 partials [T,N] ~ N(0,1), bias [N] ~ N(0, 0.1^2), residual [T,N]
+    ~ N(0,1), LayerNorm gamma [N] ~ N(1, 0.1^2) and beta [N] ~ N(0, 0.1^2),
+    drawn in that order (float32)."""
+    rng = np.random.default_rng(seed)
+    out = {"P": [rng.standard_normal((T, N), dtype=np.float32) for _ in range(n)]}
+    out["bias"] = (rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    out["residual"] = rng.standard_normal((T, N), dtype=np.float32)
+    out["gamma"] = (np.float32(1.0) + rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
+    out["beta"] = (rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
     return out
 
 

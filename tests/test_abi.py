@@ -149,6 +149,27 @@ def test_gqa_attention_validation():
 
 
 @host_only
+def test_reduce_scatter_layernorm_validation():
+    lib = tp.lib()
+    f = lib.tp_shard_reduce_scatter_layernorm
+    arr = (V * 2)(A, A)
+    ok = dict(dt=1, rows=2048, N=1024, n=2, p=arr, ldp=1024, bias=None, res=None, ldr=0, g=A, b=A,
+              eps=1e-5, ys=None, ldys=0, Y=A, ldy=1024)
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["dt"], a["rows"], a["N"], a["n"], a["p"], a["ldp"], a["bias"], a["res"], a["ldr"],
+                 a["g"], a["b"], a["eps"], a["ys"], a["ldys"], a["Y"], a["ldy"], None)
+    assert call(g=None) == -1                        # gamma required
+    assert call(eps=-1.0) == -1                      # negative eps
+    assert call(N=16384, ldp=16384, ldy=16384) == -2  # hidden size beyond the register row
+    assert call(n=0) == -1
+    assert call(p=(V * 2)(A, None)) == -1            # NULL partial
+    assert call(dt=5) == -4
+    assert call(N=1028, ldp=1028, ldy=1028) == -3    # bf16 row of 1028 is not 16-byte aligned
+    assert call(rows=0) == 0                         # nothing to do
+
+
+@host_only
 def test_shard_sum_and_backward_validation():
     lib = tp.lib()
     arr = (V * 3)(A, A, None)
