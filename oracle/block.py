@@ -263,3 +263,49 @@ def reduce_scatter_layernorm(partials, gamma, beta, eps, n, rank, bias=None, res
         raise ValueError("token count must be a multiple of the shard count")
     r = slice(rank * T // n, (rank + 1) * T // n)
     return {"Ysum": full[r], "Y": layernorm(full[r], gamma, beta, eps)}
+
+
+def cross_entropy_rows(Z, targets):
+    """Per-row softmax cross-entropy of logits Z [T, V] against target token
+    ids: loss_t = log sum_j exp(Z[t, j]) - Z[t, target_t] ("张量并行",
+    损失计算层的并行化: softmax over each row of the logits, then the
+    cross-entropy with the true token).  The log-sum-exp is evaluated with
+    the row max factored out (same value)."""
+    Z = _f64(Z)
+    m = Z.max(axis=1, keepdims=True)
+    lse = (m + np.log(np.exp(Z - m).sum(axis=1, keepdims=True)))[:, 0]
+    t = np.asarray(targets, dtype=np.int64)
+    return lse - Z[np.arange(Z.shape[0]), t]
+
+
+def vocab_shard_stats(Zi):
+    """Row statistics of one vocabulary shard's logits Zi [T, V/n]: the row
+    max m_i and s_i = sum_j exp(Zi[t, j] - m_i)."""
+    Zi = _f64(Zi)
+    m = Zi.max(axis=1)
+    return m, np.exp(Zi - m[:, None]).sum(axis=1)
+
+
+def vocab_parallel_cross_entropy(Z, targets, n):
+    """Vocabulary-parallel cross-entropy over n contiguous vocabulary shards
+    ("张量并行", 损失计算层的并行化): per shard the row statistics; their
+    combination over shards (a b*s-sized all-reduce) gives the softmax
+    denominator lse_t = M_t + log sum_i s_i exp(m_i - M_t), M_t = max_i m_i;
+    each shard's loss is the sum over the rows whose target token falls in
+    its slice of (lse_t - Z[t, target_t]); the total is the sum of the n
+    shard losses (an n-sized all-reduce).
+
+    Returns {"stats": [(m_i, s_i)], "lse": [T], "shard_loss": [n], "total",
+    "rows": per-row loss}."""
+    Z = _f64(Z)
+    T, V = Z.shape
+    if V % n:
+        raise ValueError("vocabulary size must be a multiple of the shard count")
+    w = V // n
+    t = np.asarray(targets, dtype=np.int64)
+    stats = [vocab_shard_stats(Z[:, i * w:(i + 1) * w]) for i in range(n)]
+    M = np.max(np.stack([m for m, _ in stats]), axis=0)
+    lse = M + np.log(sum(s * np.exp(m - M) for m, s in stats))
+    rows = lse - Z[np.arange(T), t]
+    shard_loss = np.array([rows[(t >= i * w) & (t < (i + 1) * w)].sum() for i in range(n)])
+    return {"stats": stats, "lse": lse, "shard_loss": shard_loss, "total": shard_loss.sum(), "rows": rows}

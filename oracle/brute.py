@@ -165,3 +165,14 @@ def layernorm(x, gamma, beta, eps):
         inv = 1.0 / math.sqrt(var + eps)
         out.append([float(gamma[j]) * (row[j] - mu) * inv + float(beta[j]) for j in range(n)])
     return out
+
+
+def cross_entropy_rows(Z, targets):
+    """Row by row: -log(exp(z_target) / sum_j exp(z_j)) with math.exp, the
+    row max subtracted first."""
+    out = []
+    for row, t in zip(_rows(Z), targets):
+        m = max(row)
+        z = sum(math.exp(v - m) for v in row)
+        out.append(-math.log(math.exp(row[int(t)] - m) / z))
+    return out
