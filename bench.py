@@ -284,6 +284,31 @@ class Rows:
                                                       eps=1e-5, bias=s["bias"], residual=s["res"][sl],
                                                       Ysum=s["Ysum"][sl])
 
+    # ---- vocabulary-parallel cross-entropy, Llama-3 vocabulary 128256 over
+    #      4 shards of 32064 columns, b 4 x s 2048 token rows; all 4 shards'
+    #      stats, the log-sum-exp combination, 4 shard losses and the total
+    def vocab_ce(self):
+        t = self.torch
+        T, V, n = 8192, 128256, 4
+        w = V // n
+        s = {"Z": [self.randn((T, w), 2.0) for _ in range(n)], "n": n, "T": T, "w": w,
+             "tg": t.randint(0, V, (T,), generator=self.g, device="cuda:0", dtype=t.int32)}
+        s["stats"] = [self.empty((T, 2), t.float32) for _ in range(n)]
+        s["lse"] = self.empty((T,), t.float32)
+        s["loss"] = [self.empty((1,), t.float32) for _ in range(n)]
+        s["total"] = self.empty((1,), t.float32)
+        s["bytes"] = 2.0 * T * V
+        return s
+
+    def vocab_ce_step(self, s):
+        tp = self.tp
+        for i in range(s["n"]):
+            tp.tp_vocab_ce_shard_stats(s["Z"][i], s["stats"][i])
+        tp.tp_vocab_ce_lse(s["stats"], s["lse"])
+        for i in range(s["n"]):
+            tp.tp_vocab_ce_shard_loss(s["Z"][i], i * s["w"], s["tg"], s["lse"], s["loss"][i])
+        tp.tp_vocab_ce_total(s["loss"], s["total"])
+
     # ---- decode GEMV: 16 tokens, h 8192, ffn 28672 / 8, all 8 shards
     #      (940 MB of weights > the 256 MB Infinity Cache: every GEMV streams from HBM)
     def decode(self):
@@ -348,6 +373,15 @@ def rows(torch, tp, steps, warmup):
                                                   "LayerNorm) per graph replay; bytes = partials + residual "
                                                   "read, fp32 sum + bf16 output written"}
     del s
+    s = R.vocab_ce()
+    gc = graph_of(torch, lambda: R.vocab_ce_step(s))
+    ms_c, _ = timed(torch, lambda kt: gc.replay(), s_ms, w_ms)
+    out["vocab_parallel_cross_entropy"] = {"ms": ms_c, "bytes": s["bytes"], "gbs": s["bytes"] / ms_c / 1e6,
+                                           "frac_hbm_peak": s["bytes"] / ms_c / 1e6 / PEAK_HBM_GBS,
+                                           "note": "4 shards x [8192 x 32064] bf16 logits: row stats, "
+                                                   "log-sum-exp, shard losses, total per graph replay; "
+                                                   "bytes = the logits read once"}
+    del s
     s = R.decode()
     gd = graph_of(torch, lambda: R.decode_step(s))
     ms_d, _ = timed(torch, lambda kt: gd.replay(), s_ms, 3)
@@ -388,6 +422,9 @@ def run_op(torch, tp, synth, name, iters):
         elif name == "c7_spln":
             s = R.sp_ln()
             fn = lambda: R.sp_ln_step(s)
+        elif name == "c8_ce":
+            s = R.vocab_ce()
+            fn = lambda: R.vocab_ce_step(s)
         elif name.startswith("c5_"):
             s = R.decode()
             k = {"c5_col": 0, "c5_row": 1}[name]

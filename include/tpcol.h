@@ -216,6 +216,48 @@ int tp_shard_reduce_scatter_layernorm(int out_dtype, int64_t rows, int64_t N, in
                                       void *Y, int64_t ldy, void *stream);
 
 /*
+ * Vocabulary-parallel cross-entropy ("张量并行", 损失计算层的并行化): the
+ * logits [T x V] are split by vocabulary columns, shard i holding columns
+ * vocab_start .. vocab_start + Vi - 1.  Instead of gathering the b*s*v
+ * logits, each shard reduces its slice of every row (step 1), the shards'
+ * row numbers are combined -- a b*s-sized all-reduce (step 2) -- giving the
+ * softmax denominator, each shard sums the loss of the rows whose target
+ * token it holds (step 3), and the n shard losses are summed -- an n-sized
+ * all-reduce (step 4).  The row statistics carry the row max next to the
+ * sum of exponentials, which keeps the same denominator within fp32 range.
+ *
+ * Step 1: stats [T x 2] fp32 = (max_j z[t][j], sum_j exp(z[t][j] - max))
+ *         over the shard's Vi columns.  logits dtype TP_F32 / TP_BF16,
+ *         row-major [T x Vi] with row stride ldz >= Vi elements; any width,
+ *         stride and element-aligned address (16-byte vectors inside rows).
+ *         A row whose values are all -inf yields (-inf, 0).
+ */
+int tp_vocab_ce_shard_stats(int dtype, int64_t T, int64_t Vi, const void *logits, int64_t ldz,
+                            float *stats, void *stream);
+/*
+ * Step 2: lse[t] = M + log sum_i s_i[t] exp(m_i[t] - M), M = max_i m_i[t]
+ *         (the row's log-sum-exp over the whole vocabulary), shards added in
+ *         index order.  stats: HOST array of n device pointers ([T x 2]).
+ */
+int tp_vocab_ce_lse(int64_t T, int n, const float *const *stats, float *lse, void *stream);
+/*
+ * Step 3: shard_loss[0] = sum over rows t whose target lies in this shard's
+ *         columns of (lse[t] - z[t][target[t] - vocab_start]) (fp32, rows
+ *         added in a fixed order).  row_loss [T] (optional) receives each
+ *         row's term, 0 for rows whose target is elsewhere.  targets: int32
+ *         token ids [T]; ids outside every shard contribute nothing.
+ */
+int tp_vocab_ce_shard_loss(int dtype, int64_t T, int64_t Vi, int64_t vocab_start,
+                           const void *logits, int64_t ldz, const int32_t *targets,
+                           const float *lse, float *row_loss, float *shard_loss, void *stream);
+/*
+ * Step 4: total[0] = sum_i shard_losses[i][0] in shard order (the summed
+ *         cross-entropy of the T rows).  shard_losses: HOST array of n
+ *         device pointers to one float each.
+ */
+int tp_vocab_ce_total(int n, const float *const *shard_losses, float *total, void *stream);
+
+/*
  * MLP shard backward given dY (broadcast to every shard):
  *   row layer    dW2_i = H_i^T dY,  dH_i = dY W2_i^T
  *   activation   dZ_i = dH_i * GELU'(Z_i)          (GELU; Z_i recomputed)

@@ -22,6 +22,7 @@ __all__ = [
     "TpError", "lib", "library_path", "TP_F32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU_ERF",
     "TP_ACT_SWIGLU", "tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_heads_shard",
     "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace", "tp_shard_reduce_scatter_layernorm",
+    "tp_vocab_ce_shard_stats", "tp_vocab_ce_lse", "tp_vocab_ce_shard_loss", "tp_vocab_ce_total",
     "tp_shard_sum", "tp_mlp_shard_backward", "tp_check_split", "tp_set_gemv_max_m",
     "tp_status_string", "tp_last_error", "tp_col_linear_gelu_workspace",
     "tp_row_linear_partial_workspace", "tp_attn_heads_shard_workspace",
@@ -53,6 +54,10 @@ _SIGS = {
     "tp_shard_reduce_scatter_layernorm": (_int, [_int, _i64, _i64, _int, ctypes.POINTER(_vp), _i64, _vp,
                                                  _vp, _i64, _vp, _vp, ctypes.c_float, _vp, _i64, _vp,
                                                  _i64, _vp]),
+    "tp_vocab_ce_shard_stats": (_int, [_int, _i64, _i64, _vp, _i64, _vp, _vp]),
+    "tp_vocab_ce_lse": (_int, [_i64, _int, ctypes.POINTER(_vp), _vp, _vp]),
+    "tp_vocab_ce_shard_loss": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "tp_vocab_ce_total": (_int, [_int, ctypes.POINTER(_vp), _vp, _vp]),
     "tp_mlp_shard_backward": (_int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp,
                                      _i64, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp,
                                      _i64, _vp, _sz, _vp]),
@@ -299,6 +304,39 @@ def tp_shard_reduce_scatter_layernorm(partials, gamma, beta, Y, eps=1e-5, bias=N
         _dtype_code(Y), rows, N, n, arr, ldp, _ptr(bias), pr, ldr, _ptr(gamma), _ptr(beta), float(eps),
         ps, lds, py, ldy, _stream(stream, Y)))
     return Y
+
+
+def tp_vocab_ce_shard_stats(logits, stats, stream=None):
+    """stats [T x 2] float32 = (row max, sum exp(z - max)) of this shard's logits."""
+    pz, T, Vi, ldz = _mat(logits, "logits")
+    _check("tp_vocab_ce_shard_stats", lib().tp_vocab_ce_shard_stats(
+        _dtype_code(logits), T, Vi, pz, ldz, stats.data_ptr(), _stream(stream, logits)))
+    return stats
+
+
+def tp_vocab_ce_lse(stats, lse, stream=None):
+    """lse [T] = log-sum-exp of each row over all shards from their stats."""
+    n = len(stats)
+    arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in stats])
+    _check("tp_vocab_ce_lse", lib().tp_vocab_ce_lse(lse.numel(), n, arr, lse.data_ptr(), _stream(stream, lse)))
+    return lse
+
+
+def tp_vocab_ce_shard_loss(logits, vocab_start, targets, lse, shard_loss, row_loss=None, stream=None):
+    """shard_loss [1] = sum over rows whose target this shard holds of lse - z_target."""
+    pz, T, Vi, ldz = _mat(logits, "logits")
+    _check("tp_vocab_ce_shard_loss", lib().tp_vocab_ce_shard_loss(
+        _dtype_code(logits), T, Vi, vocab_start, pz, ldz, targets.data_ptr(), lse.data_ptr(), _ptr(row_loss),
+        shard_loss.data_ptr(), _stream(stream, logits)))
+    return shard_loss
+
+
+def tp_vocab_ce_total(shard_losses, total, stream=None):
+    """total [1] = sum of the shards' losses, in shard order."""
+    n = len(shard_losses)
+    arr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in shard_losses])
+    _check("tp_vocab_ce_total", lib().tp_vocab_ce_total(n, arr, total.data_ptr(), _stream(stream, total)))
+    return total
 
 
 def tp_mlp_shard_backward(X, W1, W2, dY, dW1, dW2, dXi, act="gelu", Wup=None, b1=None,

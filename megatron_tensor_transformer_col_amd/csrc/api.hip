@@ -68,6 +68,25 @@ int check_vec(const void *p, int64_t n, size_t es, const char *name) {
   return check_mat(p, 1, n, n, es, name);
 }
 
+// a device array with no row-width rule: non-NULL (when required) and
+// aligned to `align` bytes
+int check_arr(const void *p, bool required, size_t align, const char *name) {
+  if (p == nullptr) return required ? fail(TP_ERR_ARG, "%s is NULL", name) : TP_OK;
+  if ((reinterpret_cast<uintptr_t>(p) % align) != 0)
+    return fail(TP_ERR_ALIGN, "%s is not %zu-byte aligned", name, align);
+  return TP_OK;
+}
+
+// a row-major matrix read element by element (any width and stride): non-NULL
+// when it has rows, element-aligned, ld >= cols
+int check_rows(const void *p, int64_t rows, int64_t cols, int64_t ld, size_t es, const char *name) {
+  if (p == nullptr) return rows > 0 ? fail(TP_ERR_ARG, "%s is NULL", name) : TP_OK;
+  if ((reinterpret_cast<uintptr_t>(p) % es) != 0) return fail(TP_ERR_ALIGN, "%s is not %zu-byte aligned", name, es);
+  if (ld < cols)
+    return fail(TP_ERR_SHAPE, "%s: leading dimension %lld < width %lld", name, (long long)ld, (long long)cols);
+  return TP_OK;
+}
+
 int check_dims(std::initializer_list<int64_t> dims, const char *what) {
   for (int64_t d : dims)
     if (d < 0 || d > kMaxDim) return fail(TP_ERR_SHAPE, "%s: dimension %lld out of range", what, (long long)d);
@@ -409,6 +428,64 @@ int tp_shard_reduce_scatter_layernorm(int out_dtype, int64_t rows, int64_t N, in
   TRY(hip_status(launch_rs_layernorm(out_dtype, rows, N, n, partials, ldp, bias, residual, ldr, gamma, beta,
                                      eps, Ysum, ldys, Y, ldy, static_cast<hipStream_t>(stream)),
                  "reduce-scatter layernorm"));
+  return ok();
+}
+
+int tp_vocab_ce_shard_stats(int dtype, int64_t T, int64_t Vi, const void *logits, int64_t ldz,
+                            float *stats, void *stream) {
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
+  TRY(check_dims({T, Vi}, "tp_vocab_ce_shard_stats"));
+  if (Vi < 1) return fail(TP_ERR_SHAPE, "Vi must be >= 1");
+  TRY(check_rows(logits, T, Vi, ldz, esize(dtype), "logits"));
+  TRY(check_arr(stats, T > 0, 8, "stats"));
+  if (T == 0) return ok();
+  TRY(hip_status(launch_vocab_stats(dtype, T, Vi, logits, ldz, stats, static_cast<hipStream_t>(stream)),
+                 "vocab stats"));
+  return ok();
+}
+
+int tp_vocab_ce_lse(int64_t T, int n, const float *const *stats, float *lse, void *stream) {
+  if (n < 1 || n > 64) return fail(TP_ERR_ARG, "shard count %d outside 1..64", n);
+  if (stats == nullptr) return fail(TP_ERR_ARG, "stats array is NULL");
+  TRY(check_dims({T}, "tp_vocab_ce_lse"));
+  for (int i = 0; i < n; ++i) {
+    char name[32];
+    snprintf(name, sizeof(name), "stats[%d]", i);
+    TRY(check_arr(stats[i], T > 0, 8, name));
+  }
+  TRY(check_arr(lse, T > 0, 4, "lse"));
+  if (T == 0) return ok();
+  TRY(hip_status(launch_vocab_lse(T, n, stats, lse, static_cast<hipStream_t>(stream)), "vocab lse"));
+  return ok();
+}
+
+int tp_vocab_ce_shard_loss(int dtype, int64_t T, int64_t Vi, int64_t vocab_start, const void *logits,
+                           int64_t ldz, const int32_t *targets, const float *lse, float *row_loss,
+                           float *shard_loss, void *stream) {
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
+  TRY(check_dims({T, Vi, vocab_start}, "tp_vocab_ce_shard_loss"));
+  if (Vi < 1) return fail(TP_ERR_SHAPE, "Vi must be >= 1");
+  TRY(check_rows(logits, T, Vi, ldz, esize(dtype), "logits"));
+  TRY(check_arr(targets, T > 0, 4, "targets"));
+  TRY(check_arr(lse, T > 0, 4, "lse"));
+  TRY(check_arr(row_loss, false, 4, "row_loss"));
+  TRY(check_arr(shard_loss, true, 4, "shard_loss"));
+  TRY(hip_status(launch_vocab_loss(dtype, T, Vi, vocab_start, logits, ldz, targets, lse, row_loss, shard_loss,
+                                   static_cast<hipStream_t>(stream)),
+                 "vocab loss"));
+  return ok();
+}
+
+int tp_vocab_ce_total(int n, const float *const *shard_losses, float *total, void *stream) {
+  if (n < 1 || n > 64) return fail(TP_ERR_ARG, "shard count %d outside 1..64", n);
+  if (shard_losses == nullptr) return fail(TP_ERR_ARG, "shard_losses array is NULL");
+  for (int i = 0; i < n; ++i) {
+    char name[40];
+    snprintf(name, sizeof(name), "shard_losses[%d]", i);
+    TRY(check_arr(shard_losses[i], true, 4, name));
+  }
+  TRY(check_arr(total, true, 4, "total"));
+  TRY(hip_status(launch_vocab_total(n, shard_losses, total, static_cast<hipStream_t>(stream)), "vocab total"));
   return ok();
 }
 

@@ -74,6 +74,13 @@ hipError_t launch_rs_layernorm(int out_dtype, int64_t rows, int64_t N, int n, co
                                const float *gamma, const float *beta, float eps, float *Ysum,
                                int64_t ldys, void *Y, int64_t ldy, hipStream_t s);
 int64_t rs_layernorm_max_n();
+hipError_t launch_vocab_stats(int dtype, int64_t T, int64_t Vi, const void *Z, int64_t ldz, float *stats,
+                              hipStream_t s);
+hipError_t launch_vocab_lse(int64_t T, int n, const float *const *stats, float *lse, hipStream_t s);
+hipError_t launch_vocab_loss(int dtype, int64_t T, int64_t Vi, int64_t v0, const void *Z, int64_t ldz,
+                             const int32_t *targets, const float *lse, float *row_loss, float *shard_loss,
+                             hipStream_t s);
+hipError_t launch_vocab_total(int n, const float *const *losses, float *total, hipStream_t s);
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,
                          hipStream_t s);
 

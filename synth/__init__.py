@@ -28,7 +28,7 @@ __all__ = [
     "Workload", "WORKLOADS", "round_to_bf16_bits", "bf16_bits_to_f32",
     "Tensor", "draw_normal", "make_mlp_inputs", "make_swiglu_inputs",
     "make_mha_inputs", "make_gqa_inputs", "column_shard", "row_shard", "qkv_shard",
-    "gqa_qkv_shard", "gqa_kv_heads_of_shard", "out_shard", "make_sp_inputs",
+    "gqa_qkv_shard", "gqa_kv_heads_of_shard", "out_shard", "make_sp_inputs", "make_ce_inputs",
 ]
 
 
@@ -91,6 +91,10 @@ WORKLOADS: Dict[str, Workload] = {
     # bias, residual and LayerNorm
     "sp_ln_gpt2m": Workload("sp_ln_gpt2m", "sp_layernorm", "f32", b=8, s=1024, h=1024,
                             n_shards=4),
+    # vocabulary-parallel cross-entropy, Llama-3 vocabulary (128256) over 4
+    # shards of 32064 columns, 8192 token rows, bf16 logits
+    "vocab_ce_bf16": Workload("vocab_ce_bf16", "vocab_ce", "bf16", b=4, s=2048, h=128256,
+                              n_shards=4),
     # decode-phase MLP shard: 16 single-token requests, memory-bound GEMV
     "decode_mlp_bf16": Workload("decode_mlp_bf16", "decode_gelu", "bf16", b=16, s=1,
                                 h=8192, ffn=28672, n_shards=8),
@@ -233,6 +237,16 @@ def make_sp_inputs(T: int, N: int, n: int, seed: int = 0):
     out["gamma"] = (np.float32(1.0) + rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
     out["beta"] = (rng.standard_normal(N, dtype=np.float32) * np.float32(0.1)).astype(np.float32)
     return out
+
+
+def make_ce_inputs(T: int, V: int, dtype: str, seed: int = 0, scale: float = 2.0,
+                   row_block: int = 1 << 30):
+    """Logits [T, V] ~ N(0, scale^2) and int32 target token ids uniform in
+    [0, V), drawn in that order."""
+    rng = np.random.default_rng(seed)
+    logits = draw_normal(rng, (T, V), scale, dtype, row_block)
+    targets = rng.integers(0, V, size=T).astype(np.int32)
+    return {"logits": logits, "targets": targets}
 
 
 # ---------------------------------------------------------------------------

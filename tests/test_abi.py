@@ -170,6 +170,22 @@ def test_reduce_scatter_layernorm_validation():
 
 
 @host_only
+def test_vocab_cross_entropy_validation():
+    lib = tp.lib()
+    assert lib.tp_vocab_ce_shard_stats(1, 64, 32064, A, 32064, None, None) == -1     # stats NULL
+    assert lib.tp_vocab_ce_shard_stats(1, 64, 32064, A, 32000, A, None) == -2       # ld < width
+    assert lib.tp_vocab_ce_shard_stats(1, 64, 17, A + 1, 17, A, None) == -3          # bf16 logits odd address
+    assert lib.tp_vocab_ce_shard_stats(1, 64, 32064, A, 32064, MIS, None) == -3     # stats misaligned
+    assert lib.tp_vocab_ce_shard_stats(1, 0, 32064, None, 32064, None, None) == 0   # empty
+    arr = (V * 2)(A, None)
+    assert lib.tp_vocab_ce_lse(64, 2, arr, A, None) == -1                           # NULL stats
+    assert lib.tp_vocab_ce_lse(64, 0, arr, A, None) == -1
+    assert lib.tp_vocab_ce_shard_loss(1, 64, 32064, -1, A, 32064, A, A, None, A, None) == -2  # vocab_start < 0
+    assert lib.tp_vocab_ce_shard_loss(1, 64, 32064, 0, A, 32064, A, A, None, None, None) == -1  # no output
+    assert lib.tp_vocab_ce_total(2, (V * 2)(A, None), A, None) == -1
+
+
+@host_only
 def test_shard_sum_and_backward_validation():
     lib = tp.lib()
     arr = (V * 3)(A, A, None)
