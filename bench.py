@@ -172,7 +172,7 @@ def headline(torch, tp, synth, steps, warmup):
     return {
         "ms": ms, "tflops": step_flops / (ms * 1e-3) / 1e12, "step_flops": step_flops,
         "col_ms": col_ms, "col_tflops": hl.gemm_flops / (col_ms * 1e-3) / 1e12,
-        "gemm_flops": hl.gemm_flops,
+        "gemm_flops": hl.gemm_flops, "col_bytes": 2.0 * (hl.T * hl.h + hl.h * hl.f + hl.T * hl.f),
         "config": {"workload": "gpt2m_mlp_bf16: TP MLP layer, tokens 8x1024, h 1024, ffn 4096, "
                                "4 shards in sequence + shard sum",
                    "tokens": hl.T, "h": hl.h, "ffn": hl.W.ffn, "n_shards": hl.n,
@@ -454,6 +454,31 @@ def run_op(torch, tp, synth, name, iters):
                       "wall_s": time.perf_counter() - t0}), flush=True)
 
 
+# --------------------------------------------------------------------------- HBM traffic
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_col_gelu_gpt2m_shard.md")
+TRAFFIC_SOURCES = ["gemm_lds.hip", "gemm_common.hpp", "device_common.hpp", "lds_dma.hpp"]
+
+
+def col_gemm_traffic():
+    """HBM bytes per launch of the column GEMM from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE record (KiB per dispatch, scaled by the factors a
+    1 GiB copy gave), or None when the record is missing or the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    try:
+        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-record:"))
+        rec = json.loads(line.split(":", 1)[1])
+        h = hashlib.sha256()
+        for f in TRAFFIC_SOURCES:
+            with open(os.path.join(ROOT, "megatron_tensor_transformer_col_amd", "csrc", f), "rb") as fh:
+                h.update(fh.read())
+    except (OSError, StopIteration, ValueError):
+        return None
+    if h.hexdigest() != rec.get("sources_sha256"):
+        return None
+    return 1024.0 * (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"])
+
+
 # --------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(synth, seconds):
     import oracle
@@ -508,8 +533,9 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU epilogue (gemm_lds_kernel NN, 128x256 tile)",
                      "achieved": round(hl["col_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(hl["col_tflops"] / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_launch_us": round(hl["col_ms"] * 1e3, 3),
-                     "flops_per_launch": hl["gemm_flops"]},
+                     "traffic": col_gemm_traffic(), "traffic_unit": "HBM bytes per launch (rocprofv3 "
+                     "FETCH_SIZE + WRITE_SIZE, copy-calibrated)", "avg_launch_us": round(hl["col_ms"] * 1e3, 3),
+                     "flops_per_launch": hl["gemm_flops"], "algorithmic_bytes_per_launch": hl["col_bytes"]},
         "frac_peak": round(hl["tflops"] / PEAK_BF16_TFLOPS, 4),
     }
     if not args.no_rows:
