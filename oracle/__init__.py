@@ -29,6 +29,6 @@ from .block import (  # noqa: F401
     gelu, gelu_grad, silu, silu_grad, softmax_rows,
     linear, row_partial, shard_sum,
     mlp_gelu, mlp_swiglu, mlp_gelu_backward, mlp_swiglu_backward,
-    attention_heads, mha, mha_gqa, layernorm, reduce_scatter_layernorm,
+    attention_heads, mha, mha_gqa, attention_head_backward, mha_backward, layernorm, reduce_scatter_layernorm,
     cross_entropy_rows, vocab_shard_stats, vocab_parallel_cross_entropy,
 )

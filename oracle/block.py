@@ -236,6 +236,86 @@ def mha_gqa(X, Wq, Wk, Wv, Wo, heads, kv_heads, b, s, causal=True):
     return {"Q": Q, "K": K, "V": V, "O": O, "Y": O @ Wo}
 
 
+def attention_head_backward(Q, K, V, dO, causal):
+    """Gradients of L = <O, dO> for one head, O = softmax(Q K^T / sqrt(d)
+    [+ causal mask]) V.  The pages stop at the forward ("张量并行", Multi-Head
+    Attention 的并行化: heads are independent, so a shard differentiates its
+    own heads); the backward is the chain rule through the two products and
+    the row softmax, whose Jacobian is diag(p) - p p^T:
+
+        dV = P^T dO,   dP = dO V^T,
+        dS = P * (dP - D),  D_i = sum_j P_ij dP_ij  (= sum_c dO_ic O_ic),
+        dQ = dS K / sqrt(d),   dK = dS^T Q / sqrt(d).
+
+    Masked entries have P = 0 and so dS = 0.  Also returns P, O, D and lse,
+    the natural log of each row's softmax denominator sum_j exp(S_ij) of the
+    scaled scores S = Q K^T / sqrt(d)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    d = Q.shape[1]
+    S = (Q @ K.T) / np.sqrt(d)
+    if causal:
+        S = np.where(np.triu(np.ones(S.shape, dtype=bool), k=1), -np.inf, S)
+    P = softmax_rows(S)
+    m = S.max(axis=1)
+    lse = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    O = P @ V
+    dP = dO @ V.T
+    D = (dP * P).sum(axis=1)
+    dS = P * (dP - D[:, None])
+    return {"P": P, "O": O, "lse": lse, "D": D, "dS": dS, "dV": P.T @ dO,
+            "dQ": dS @ K / np.sqrt(d), "dK": dS.T @ Q / np.sqrt(d)}
+
+
+def mha_backward(X, Wq, Wk, Wv, Wo, dY, heads, b, s, causal=True, kv_heads=None, head_dim=None):
+    """Gradients of L = <Y, dY> for the unsharded (grouped-query) attention
+    block Y = [O_1 ... O_H] Wo, O_t = Attention(X Wq^(t), X Wk^(u), X Wv^(u)),
+    u = t // g, g = heads / kv_heads (kv_heads = heads: multi-head).
+
+    Output projection, a row-wise layer (Infra: Tensor Parallel, Row-wise TP
+    backward): dWo = O^T dY, dO = dY Wo^T.  Per head ``attention_head_backward``;
+    a kv head read by g query heads receives the sum of their dK / dV.
+    QKV projection, a column-wise layer (Infra: Tensor Parallel, Column-wise
+    TP backward): dWq = X^T dQ, dWk = X^T dK, dWv = X^T dV,
+    dX = dQ Wq^T + dK Wk^T + dV Wv^T.
+
+    ``heads`` counts the query heads in Wq's columns; d = h / heads unless
+    ``head_dim`` is given (a shard's subset of the heads: d = head_dim, Wq
+    holding heads * d columns).  Token-major results ([b*s, ...]); lse and D
+    are [b*s, heads]."""
+    X, Wq, Wk, Wv, Wo, dY = (_f64(a) for a in (X, Wq, Wk, Wv, Wo, dY))
+    kv_heads = heads if kv_heads is None else kv_heads
+    h = X.shape[1]
+    if (head_dim is None and h % heads) or heads % kv_heads:
+        raise ValueError("heads must divide h and be a multiple of kv_heads")
+    d = h // heads if head_dim is None else head_dim
+    if Wq.shape[1] != heads * d or Wk.shape[1] != kv_heads * d or Wv.shape[1] != kv_heads * d:
+        raise ValueError("Wq needs heads * d columns, Wk / Wv kv_heads * d")
+    g = heads // kv_heads
+    Q, K, V = X @ Wq, X @ Wk, X @ Wv
+    O = np.zeros((b * s, heads * d))
+    lse = np.zeros((b * s, heads))
+    D = np.zeros((b * s, heads))
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    # O is needed before dO = dY Wo^T can be split per head; dO itself only
+    # needs dY and Wo.
+    dO = dY @ Wo.T
+    for bi in range(b):
+        r = slice(bi * s, (bi + 1) * s)
+        for t in range(heads):
+            u = t // g
+            cq, ckv = slice(t * d, (t + 1) * d), slice(u * d, (u + 1) * d)
+            gr = attention_head_backward(Q[r, cq], K[r, ckv], V[r, ckv], dO[r, cq], causal)
+            O[r, cq] = gr["O"]
+            lse[r, t] = gr["lse"]
+            D[r, t] = gr["D"]
+            dQ[r, cq] = gr["dQ"]
+            dK[r, ckv] += gr["dK"]
+            dV[r, ckv] += gr["dV"]
+    return {"Q": Q, "K": K, "V": V, "O": O, "Y": O @ Wo, "lse": lse, "D": D, "dO": dO,
+            "dQ": dQ, "dK": dK, "dV": dV, "dWo": O.T @ dY, "dWq": X.T @ dQ, "dWk": X.T @ dK,
+            "dWv": X.T @ dV, "dX": dQ @ Wq.T + dK @ Wk.T + dV @ Wv.T}
+
+
 def layernorm(x, gamma, beta, eps):
     """LN(x) = gamma * (x - mu(x)) / sqrt(sigma^2(x) + eps) + beta over the
     last (hidden) dimension, mu and sigma^2 the mean and the population
