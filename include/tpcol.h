@@ -126,7 +126,10 @@ size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t
  *   Wo   [heads_local*d x h]            ldwo   bf16
  *   P    [b*s x h]                      ldp    float32 (output)
  *   ws   tp_attn_heads_shard_workspace() bytes: QKV_i [b*s x 3*hl*d] then
- *        O_i [b*s x hl*d], both bf16 row-major, readable after the call.
+ *        O_i [b*s x hl*d], both bf16 row-major, readable after the call,
+ *        then each query row's softmax statistic (fp32 [b][hl][s], log2 of
+ *        sum_j exp2(S_ij log2(e)) for the scaled scores S), which
+ *        tp_attn_shard_backward reads.
  * Only TP_BF16 and d == 128 are supported (TP_ERR_DTYPE / TP_ERR_SHAPE);
  * 3*heads_local*d must not exceed 2^24 (TP_ERR_SHAPE).
  */
@@ -152,7 +155,8 @@ size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s,
  *   Wqkv [h x (heads_local + 2*kv_heads_local)*d]: Q heads, then K heads,
  *        then V heads, head u at offset u*d inside its block.
  *   ws   tp_attn_gqa_shard_workspace() bytes: QKV_i [b*s x (hl + 2*kvl)*d]
- *        then O_i [b*s x hl*d], bf16 row-major, readable after the call.
+ *        then O_i [b*s x hl*d], bf16 row-major, readable after the call,
+ *        then the per-row softmax statistic as for tp_attn_heads_shard.
  * heads_local must be a multiple of kv_heads_local, and
  * (heads_local + 2*kv_heads_local)*d at most 2^24 (TP_ERR_SHAPE); otherwise
  * as tp_attn_heads_shard.
@@ -166,6 +170,45 @@ int tp_attn_gqa_shard(int dtype, int64_t b, int64_t s, int64_t h,
                       void *ws, size_t ws_bytes, void *stream);
 size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
                                    int64_t kv_heads_local, int64_t d);
+
+/*
+ * Backward of the attention shard (multi-head: kv_heads_local ==
+ * heads_local; grouped-query otherwise), given dY = dL/dY broadcast to every
+ * shard.  A shard owns whole heads, so it differentiates them alone
+ * ("张量并行", Multi-Head Attention 的并行化); the projections follow the
+ * row- and column-wise backward equations of "Infra: Tensor Parallel":
+ *   output projection (row-wise)  dWo_i = O_i^T dY,  dO_i = dY Wo_i^T
+ *   per head (chain rule through the products and the row softmax)
+ *                                 dV = P^T dO,  dS = P * (dO V^T - rowsum(dO*O)),
+ *                                 dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d)
+ *                                 (a kv head sums its query heads' dK, dV)
+ *   QKV projection (column-wise)  dWqkv_i = X^T [dQ | dK | dV],
+ *                                 dX_i = [dQ | dK | dV] Wqkv_i^T
+ * dX_i is this shard's partial of dX = sum_i dX_i (f's backward all-reduce;
+ * tp_shard_sum).
+ *   X, Wqkv, Wo, dY: as in the forward call (bf16); dY [b*s x h] lddy.
+ *   fwd_ws: the workspace of the forward call (tp_attn_heads_shard or
+ *        tp_attn_gqa_shard) on the same inputs, as it left it: QKV_i, O_i
+ *        and the row statistic are read, not recomputed.
+ *   Outputs (float32, dense unless noted): dWqkv [h x (hl + 2*kvl)*d],
+ *        dWo [hl*d x h], dXi [b*s x h] with row stride lddx.
+ *   ws   tp_attn_shard_backward_workspace() bytes: dO_i (bf16), D (fp32),
+ *        [dQ | dK | dV] (bf16, packed like QKV_i).
+ * bf16 and d == 128 only; shape rules as for tp_attn_gqa_shard.  Both
+ * workspaces 256-byte aligned.  Every sum runs in a fixed order: repeated
+ * calls give identical bits.
+ */
+int tp_attn_shard_backward(int dtype, int64_t b, int64_t s, int64_t h,
+                           int64_t heads_local, int64_t kv_heads_local, int64_t d, int causal,
+                           const void *X, int64_t ldx,
+                           const void *Wqkv, int64_t ldwqkv,
+                           const void *Wo, int64_t ldwo,
+                           const void *dY, int64_t lddy,
+                           const void *fwd_ws, size_t fwd_ws_bytes,
+                           float *dWqkv, float *dWo, float *dXi, int64_t lddx,
+                           void *ws, size_t ws_bytes, void *stream);
+size_t tp_attn_shard_backward_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
+                                        int64_t kv_heads_local, int64_t d);
 
 /*
  * Sum of the N shard partials, added in shard order in float32, plus an

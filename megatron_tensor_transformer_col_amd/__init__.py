@@ -21,7 +21,8 @@ import threading
 __all__ = [
     "TpError", "lib", "library_path", "TP_F32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU_ERF",
     "TP_ACT_SWIGLU", "tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_heads_shard",
-    "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace", "tp_shard_reduce_scatter_layernorm",
+    "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace", "tp_attn_shard_backward",
+    "tp_attn_shard_backward_workspace", "tp_shard_reduce_scatter_layernorm",
     "tp_vocab_ce_shard_stats", "tp_vocab_ce_lse", "tp_vocab_ce_shard_loss", "tp_vocab_ce_total",
     "tp_shard_sum", "tp_mlp_shard_backward", "tp_check_split", "tp_set_gemv_max_m",
     "tp_status_string", "tp_last_error", "tp_col_linear_gelu_workspace",
@@ -49,6 +50,9 @@ _SIGS = {
     "tp_attn_gqa_shard": (_int, [_int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp,
                                  _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "tp_attn_gqa_shard_workspace": (_sz, [_int, _i64, _i64, _i64, _i64, _i64]),
+    "tp_attn_shard_backward": (_int, [_int, _i64, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp, _i64,
+                                      _vp, _i64, _vp, _i64, _vp, _sz, _vp, _vp, _vp, _i64, _vp, _sz, _vp]),
+    "tp_attn_shard_backward_workspace": (_sz, [_int, _i64, _i64, _i64, _i64, _i64]),
     "tp_shard_sum": (_int, [_int, _i64, _i64, _int, ctypes.POINTER(_vp), _i64, _vp, _vp, _i64,
                             _vp]),
     "tp_shard_reduce_scatter_layernorm": (_int, [_int, _i64, _i64, _int, ctypes.POINTER(_vp), _i64, _vp,
@@ -264,6 +268,36 @@ def tp_attn_gqa_shard(X, Wqkv, Wo, P, b, s, heads_local, kv_heads_local, d=128, 
         dt, b, s, h, heads_local, kv_heads_local, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo,
         pp, ldp, pws, nws, _stream(stream, X)))
     return P
+
+
+def tp_attn_shard_backward_workspace(dtype, b, s, heads_local, kv_heads_local, d=128):
+    return lib().tp_attn_shard_backward_workspace(dtype, b, s, heads_local, kv_heads_local, d)
+
+
+def tp_attn_shard_backward(X, Wqkv, Wo, dY, fwd_ws, dWqkv, dWo, dXi, b, s, heads_local, kv_heads_local=None,
+                           d=128, causal=True, ws=None, stream=None):
+    """Backward of the attention shard: dWqkv = X^T [dQ|dK|dV], dWo = O^T dY
+    (float32, dense) and this shard's partial dXi (float32).  ``fwd_ws`` is
+    the uint8 workspace tensor the forward call (tp_attn_heads_shard /
+    tp_attn_gqa_shard with the same inputs) wrote; it must be passed to the
+    forward explicitly so that it survives until here."""
+    kvl = heads_local if kv_heads_local is None else kv_heads_local
+    dt = _dtype_code(X)
+    px, _, h, ldx = _mat(X, "X")
+    pq, _, _, ldq = _mat(Wqkv, "Wqkv")
+    po, _, _, ldo = _mat(Wo, "Wo")
+    py, _, _, ldy = _mat(dY, "dY")
+    pd, _, _, lddx = _mat(dXi, "dXi")
+    for t, name in ((dWqkv, "dWqkv"), (dWo, "dWo")):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be dense")
+    need = tp_attn_shard_backward_workspace(dt, b, s, heads_local, kvl, d)
+    pws, nws = _workspace(ws, need, X.device, zeroed=False)
+    _check("tp_attn_shard_backward", lib().tp_attn_shard_backward(
+        dt, b, s, h, heads_local, kvl, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo, py, ldy,
+        fwd_ws.data_ptr(), fwd_ws.numel() * fwd_ws.element_size(), dWqkv.data_ptr(), dWo.data_ptr(), pd, lddx,
+        pws, nws, _stream(stream, X)))
+    return dWqkv, dWo, dXi
 
 
 def tp_shard_sum(partials, Y, bias=None, stream=None):

@@ -124,15 +124,33 @@ BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
   return w;
 }
 
+// forward workspace: packed QKV_i, O_i (bf16) and the per-row softmax
+// statistic (fp32 [b][hl][s]) the backward reads
 struct AttnWs {
-  size_t qkv, o, total;
+  size_t qkv, o, lse, total;
 };
 AttnWs attn_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
   const size_t T = (size_t)b * (size_t)s;
   AttnWs w;
   w.qkv = 0;
   w.o = round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
-  w.total = w.o + round256(T * (size_t)hl * (size_t)d * 2);
+  w.lse = w.o + round256(T * (size_t)hl * (size_t)d * 2);
+  w.total = w.lse + round256(T * (size_t)hl * 4);
+  return w;
+}
+
+// backward workspace: dO_i (bf16 [T x hl*d]), D (fp32 [b][hl][s]) and
+// dQKV_i (bf16, packed like QKV_i)
+struct AttnBwdWs {
+  size_t dO, D, dqkv, total;
+};
+AttnBwdWs attn_bwd_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
+  const size_t T = (size_t)b * (size_t)s;
+  AttnBwdWs w;
+  w.dO = 0;
+  w.D = round256(T * (size_t)hl * (size_t)d * 2);
+  w.dqkv = w.D + round256(T * (size_t)hl * 4);
+  w.total = w.dqkv + round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
   return w;
 }
 
@@ -170,6 +188,7 @@ int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, in
   char *base = static_cast<char *>(ws);
   void *qkv = base + L.qkv;
   void *O = base + L.o;
+  float *lse = reinterpret_cast<float *>(base + L.lse);
 
   GemmArgs q;
   q.dtype = DT_BF16;
@@ -180,7 +199,7 @@ int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, in
   q.B = Wqkv; q.ldb = ldwqkv;
   q.C = qkv; q.ldc = wqkv;
   TRY(hip_status(launch_gemm(q, st), "QKV GEMM"));
-  TRY(hip_status(launch_flash_attn(qkv, wqkv, O, w, b, s_len, heads_local, kv_heads_local, d,
+  TRY(hip_status(launch_flash_attn(qkv, wqkv, O, w, lse, b, s_len, heads_local, kv_heads_local, d,
                                    causal != 0, st),
                  "attention"));
   GemmArgs o;
@@ -192,6 +211,101 @@ int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, in
   o.B = Wo; o.ldb = ldwo;
   o.C = P; o.ldc = ldp;
   TRY(hip_status(launch_gemm(o, st), "output GEMM"));
+  return ok();
+}
+
+int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
+                  int64_t kv_heads_local, int64_t d, int causal, const void *X, int64_t ldx,
+                  const void *Wqkv, int64_t ldwqkv, const void *Wo, int64_t ldwo, const void *dY,
+                  int64_t lddy, const void *fwd_ws, size_t fwd_ws_bytes, float *dWqkv, float *dWo,
+                  float *dXi, int64_t lddx, void *ws, size_t ws_bytes, void *stream) {
+  const char *fn = "tp_attn_shard_backward";
+  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports bf16 only");
+  TRY(check_dims({b, s_len, h, heads_local, kv_heads_local, d}, fn));
+  if (h < 1 || heads_local < 1) return fail(TP_ERR_SHAPE, "h and heads_local must be >= 1");
+  if (kv_heads_local < 1 || heads_local % kv_heads_local)
+    return fail(TP_ERR_SHAPE, "heads_local %lld is not a multiple of kv_heads_local %lld",
+                (long long)heads_local, (long long)kv_heads_local);
+  if (d != 128) return fail(TP_ERR_SHAPE, "head dim %lld unsupported (128 only)", (long long)d);
+  const int64_t T = b * s_len;
+  if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
+  const int64_t w = heads_local * d;
+  const int64_t wqkv = (heads_local + 2 * kv_heads_local) * d;
+  if (wqkv > (int64_t(1) << 24))
+    return fail(TP_ERR_SHAPE, "(heads_local + 2*kv_heads_local)*d must be <= 2^24");
+  TRY(check_mat(X, T, h, ldx, 2, "X"));
+  TRY(check_mat(Wqkv, h, wqkv, ldwqkv, 2, "Wqkv"));
+  TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));
+  TRY(check_mat(dY, T, h, lddy, 2, "dY"));
+  TRY(check_mat(dWqkv, h, wqkv, wqkv, 4, "dWqkv"));
+  TRY(check_mat(dWo, w, h, h, 4, "dWo"));
+  TRY(check_mat(dXi, T, h, lddx, 4, "dXi"));
+  if (dWqkv == nullptr || dWo == nullptr) return fail(TP_ERR_ARG, "dWqkv and dWo are required");
+  const AttnWs F = attn_ws(b, s_len, heads_local, kv_heads_local, d);
+  const AttnBwdWs L = attn_bwd_ws(b, s_len, heads_local, kv_heads_local, d);
+  if (T > 0) {
+    if (fwd_ws == nullptr || fwd_ws_bytes < F.total)
+      return fail(TP_ERR_WORKSPACE, "the forward's workspace (%zu bytes) is required, got %zu", F.total,
+                  fwd_ws_bytes);
+    if (ws == nullptr || ws_bytes < L.total)
+      return fail(TP_ERR_WORKSPACE, "attention backward needs %zu workspace bytes, got %zu", L.total, ws_bytes);
+    if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || (reinterpret_cast<uintptr_t>(fwd_ws) & 255u) != 0)
+      return fail(TP_ERR_ALIGN, "workspaces must be 256-byte aligned");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const char *fb = static_cast<const char *>(fwd_ws);
+  const void *qkv = fb + F.qkv;
+  const void *O = fb + F.o;
+  const float *lse = reinterpret_cast<const float *>(fb + F.lse);
+  char *base = static_cast<char *>(ws);
+  void *dO = base + L.dO;
+  float *Dr = reinterpret_cast<float *>(base + L.D);
+  void *dqkv = base + L.dqkv;
+
+  if (T > 0) {
+    // dO_i = dY Wo_i^T  (row-parallel output projection, input gradient)
+    GemmArgs a;
+    a.dtype = DT_BF16; a.layout = LAY_NT; a.epi = EPI_STORE;
+    a.M = T; a.N = w; a.K = h;
+    a.A = dY; a.lda = lddy;
+    a.B = Wo; a.ldb = ldwo;
+    a.C = dO; a.ldc = w;
+    TRY(hip_status(launch_gemm(a, st), "dO GEMM"));
+  }
+  // dWo_i = O_i^T dY  (row-parallel weight gradient)
+  {
+    GemmArgs g;
+    g.dtype = DT_BF16; g.layout = LAY_TN; g.epi = EPI_STORE_F32;
+    g.M = w; g.N = h; g.K = T;
+    g.A = O; g.lda = w;
+    g.B = dY; g.ldb = lddy;
+    g.C = dWo; g.ldc = h;
+    TRY(hip_status(launch_gemm(g, st), "dWo GEMM"));
+  }
+  if (T > 0)
+    TRY(hip_status(launch_attn_bwd(qkv, wqkv, O, w, lse, dO, w, Dr, dqkv, b, s_len, heads_local,
+                                   kv_heads_local, d, causal != 0, st),
+                   "attention backward"));
+  // dWqkv_i = X^T dQKV_i  (column-parallel weight gradient)
+  {
+    GemmArgs g;
+    g.dtype = DT_BF16; g.layout = LAY_TN; g.epi = EPI_STORE_F32;
+    g.M = h; g.N = wqkv; g.K = T;
+    g.A = X; g.lda = ldx;
+    g.B = dqkv; g.ldb = wqkv;
+    g.C = dWqkv; g.ldc = wqkv;
+    TRY(hip_status(launch_gemm(g, st), "dWqkv GEMM"));
+  }
+  if (T > 0) {
+    // dX_i = dQKV_i Wqkv_i^T  (this shard's partial of dX)
+    GemmArgs x;
+    x.dtype = DT_BF16; x.layout = LAY_NT; x.epi = EPI_STORE_F32;
+    x.M = T; x.N = h; x.K = wqkv;
+    x.A = dqkv; x.lda = wqkv;
+    x.B = Wqkv; x.ldb = ldwqkv;
+    x.C = dXi; x.ldc = lddx;
+    TRY(hip_status(launch_gemm(x, st), "dX GEMM"));
+  }
   return ok();
 }
 
@@ -250,6 +364,22 @@ size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s, int64_t he
   (void)dtype;
   if (b < 0 || s < 0 || heads_local < 0 || d < 0) return 0;
   return attn_ws(b, s, heads_local, heads_local, d).total;
+}
+
+size_t tp_attn_shard_backward_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
+                                        int64_t kv_heads_local, int64_t d) {
+  (void)dtype;
+  if (b < 0 || s < 0 || heads_local < 0 || kv_heads_local < 0 || d < 0) return 0;
+  return attn_bwd_ws(b, s, heads_local, kv_heads_local, d).total;
+}
+
+int tp_attn_shard_backward(int dtype, int64_t b, int64_t s, int64_t h, int64_t heads_local,
+                           int64_t kv_heads_local, int64_t d, int causal, const void *X, int64_t ldx,
+                           const void *Wqkv, int64_t ldwqkv, const void *Wo, int64_t ldwo, const void *dY,
+                           int64_t lddy, const void *fwd_ws, size_t fwd_ws_bytes, float *dWqkv, float *dWo,
+                           float *dXi, int64_t lddx, void *ws, size_t ws_bytes, void *stream) {
+  return attn_bwd_impl(dtype, b, s, h, heads_local, kv_heads_local, d, causal, X, ldx, Wqkv, ldwqkv, Wo, ldwo,
+                       dY, lddy, fwd_ws, fwd_ws_bytes, dWqkv, dWo, dXi, lddx, ws, ws_bytes, stream);
 }
 
 size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,

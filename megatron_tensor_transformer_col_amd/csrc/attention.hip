@@ -92,6 +92,7 @@ struct FaArgs {
   int s, hl, nqb, items;  // items: workgroups per (sequence, head)
   int kvl, group;         // key/value heads in the shard; query heads per kv head
   float scale_log2;       // log2(e) / sqrt(d)
+  float *lse;             // [b][hl][s]: log2 of each row's softmax denominator, or NULL
 };
 
 template <bool CAUSAL>
@@ -333,6 +334,8 @@ struct FaBlock {
         const float l = sum_xor32(sum_xor16(lsum[qt] * a0 + l1 * a1));
         const int q = q_w + qt * 16 + l16;
         const float inv = 1.0f / l;
+        // the backward recomputes P = exp2(S log2(e)/sqrt(d) - lse2) from this
+        if (a.lse != nullptr && g == 0 && q < a.s) a.lse[((int64_t)bi * a.hl + head) * a.s + q] = m + log2f(l);
         uint16_t *orow = a.O + (tok0 + q) * a.ldo + head * FA_D;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -386,7 +389,7 @@ __global__ void __launch_bounds__(FA_NW * 64) flash_attn_kernel(FaArgs a) {
   }
 }
 
-hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, int64_t b,
+hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, float *lse, int64_t b,
                              int64_t s, int64_t heads_local, int64_t kv_heads_local, int64_t d,
                              bool causal, hipStream_t st) {
   if (b <= 0 || s <= 0 || heads_local <= 0) return hipSuccess;
@@ -398,6 +401,7 @@ hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ld
   a.ldq = ldqkv;
   a.O = static_cast<uint16_t *>(O);
   a.ldo = ldo;
+  a.lse = lse;
   a.s = (int)s;
   a.hl = (int)heads_local;
   a.kvl = (int)kv_heads_local;

@@ -64,9 +64,17 @@ hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const fl
                             int64_t ldp, const float *bias, void *Y, int64_t ldy, hipStream_t s);
 
 // Head-local flash attention over a packed [Q|K|V] buffer (bf16, d = 128).
-hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, int64_t b,
+// lse (optional, [b][heads_local][s] fp32): log2 of each query row's softmax
+// denominator in the scaled-score base-2 domain, for the backward
+hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ldo, float *lse, int64_t b,
                              int64_t s, int64_t heads_local, int64_t kv_heads_local, int64_t d,
                              bool causal, hipStream_t st);
+// Attention backward from the forward's packed QKV, O and lse: D (fp32
+// [b][heads_local][s], written) then dQ | dK | dV into dqkv (bf16, same
+// packing and stride as qkv)
+hipError_t launch_attn_bwd(const void *qkv, int64_t ldqkv, const void *O, int64_t ldo, const float *lse,
+                           const void *dO, int64_t lddo, float *Dr, void *dqkv, int64_t b, int64_t s,
+                           int64_t heads_local, int64_t kv_heads_local, int64_t d, bool causal, hipStream_t st);
 
 // db[n] = sum_m dZ[m][n] (dZ dtype, db float32).
 hipError_t launch_rs_layernorm(int out_dtype, int64_t rows, int64_t N, int n, const float *const *parts,

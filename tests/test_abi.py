@@ -57,9 +57,13 @@ def test_gemv_threshold_option():
 
 
 def test_workspace_sizes():
-    # attention: QKV [T x 3 hl d] + O [T x hl d] bf16, 256-byte aligned regions
+    # attention: QKV [T x 3 hl d] + O [T x hl d] bf16 + row statistic [b hl s] fp32,
+    # 256-byte aligned regions
     T = 4 * 2048
-    assert tp.tp_attn_heads_shard_workspace(1, 4, 2048, 8, 128) == T * 3 * 1024 * 2 + T * 1024 * 2
+    assert tp.tp_attn_heads_shard_workspace(1, 4, 2048, 8, 128) == T * 3 * 1024 * 2 + T * 1024 * 2 + T * 8 * 4
+    assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 2, 128) == T * 12 * 128 * 2 + T * 1024 * 2 + T * 8 * 4
+    # attention backward: dO [T x hl d] bf16 + D [b hl s] fp32 + dQKV bf16
+    assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 128) == T * 1024 * 2 + T * 8 * 4 + T * 12 * 128 * 2
     # backward: dH, H, dZ (GELU) / dH, H, [dZg | dZu] (SwiGLU)
     assert tp.tp_mlp_shard_backward_workspace(1, 1, 8192, 1024) == 3 * 8192 * 1024 * 2
     assert tp.tp_mlp_shard_backward_workspace(1, 2, 8192, 3584) == 4 * 8192 * 3584 * 2
@@ -144,7 +148,7 @@ def test_gqa_attention_validation():
     assert g(1, 4, 2048, 4096, 8, 2, 128, 1, A, 4096, A, 1024, A, 4096, A, 4096, A, 1 << 30, None) == -2
     # workspace: QKV block (hl + 2 kvl) d wide, then O
     T = 4 * 2048
-    assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 2, 128) == T * 1536 * 2 + T * 1024 * 2
+    assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 2, 128) == T * 1536 * 2 + T * 1024 * 2 + T * 8 * 4
     assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 8, 128) == tp.tp_attn_heads_shard_workspace(1, 4, 2048, 8, 128)
 
 
@@ -198,3 +202,28 @@ def test_shard_sum_and_backward_validation():
     assert bw(1, 0, 64, 256, 128, *common, A, 1 << 30, None) == -1               # act NONE
     assert bw(1, 1, 64, 256, 128, *common, A, 100, None) == -5                   # tiny workspace
     assert bw(1, 2, 64, 256, 128, *common, A, 1 << 30, None) == -1               # SwiGLU w/o Wup
+
+
+@host_only
+def test_attention_backward_validation():
+    lib = tp.lib()
+    g = lib.tp_attn_shard_backward
+    T = 4 * 2048
+    fw = tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 2, 128)
+    bw = tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 128)
+
+    def call(dt=1, hl=8, kvl=2, d=128, X=A, dWqkv=A, dWo=A, dX=A, fws=A, fwn=fw, ws=A, wsn=bw, ldwqkv=1536):
+        return g(dt, 4, 2048, 4096, hl, kvl, d, 1, X, 4096, A, ldwqkv, A, 4096, A, 4096, fws, fwn, dWqkv, dWo, dX,
+                 4096, ws, wsn, None)
+
+    assert call(dt=0) == -4                        # fp32 attention is not supported
+    assert call(kvl=3) == -2                       # 8 query heads do not group over 3 kv heads
+    assert call(d=64) == -2                        # head dim 128 only
+    assert call(ldwqkv=1024) == -2                 # ld < (hl + 2 kvl) d
+    assert call(X=None) == -1
+    assert call(dWo=None) == -1
+    assert call(dWqkv=MIS) == -3
+    assert call(fws=None) == -5                    # the forward's workspace is required
+    assert call(fwn=fw - 256) == -5
+    assert call(wsn=bw - 1) == -5
+    assert call(ws=A + 16) == -3                   # workspace not 256-byte aligned

@@ -14,7 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "megatron_tensor_transformer_col_amd", "csrc")
-SOURCES = ["attention.hip", "gemv.hip", "gemm_lds.hip"]
+SOURCES = ["attention.hip", "attn_bwd.hip", "gemv.hip", "gemm_lds.hip"]
 WAIT_STATES = 5
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
