@@ -244,6 +244,35 @@ class Rows:
         self.tp.tp_attn_heads_shard(s["X"], s["Wqkv"], s["Wo"], s["P"], b, sq, hl, dh, causal=True,
                                     ws=s["ws"])
 
+    # ---- head-sharded MHA backward (same shard): the forward once to fill
+    #      its workspace, then dY -> dWqkv, dWo, dX_i per timed call
+    def mha_bwd(self, kvl=None):
+        t = self.torch
+        s = self.mha() if kvl is None else self.gqa()
+        if kvl is None:
+            b, sq, hl, dh = s["dims"]
+            kv = hl
+            self.attn(s)
+        else:
+            b, sq, hl, kv, dh = s["dims"]
+            self.gqa_attn(s)
+        T, h = b * sq, s["X"].shape[1]
+        s["bdims"] = (b, sq, hl, kv, dh)
+        s["dY"] = self.randn((T, h), 1.0)
+        s["dWqkv"] = self.empty(tuple(s["Wqkv"].shape), t.float32)
+        s["dWo"] = self.empty(tuple(s["Wo"].shape), t.float32)
+        s["dX"] = self.empty((T, h), t.float32)
+        s["bws"] = self.empty((self.tp.tp_attn_shard_backward_workspace(1, b, sq, hl, kv, dh),), t.uint8)
+        n3 = (hl + 2 * kv) * dh
+        s["flop_bwd_gemm"] = 2.0 * T * h * hl * dh * 2 + 2.0 * T * h * n3 * 2
+        s["flop_bwd_att"] = 2.5 * 4.0 * dh * (sq * (sq + 1) / 2) * b * hl
+        return s
+
+    def attn_bwd(self, s):
+        b, sq, hl, kv, dh = s["bdims"]
+        self.tp.tp_attn_shard_backward(s["X"], s["Wqkv"], s["Wo"], s["dY"], s["ws"], s["dWqkv"], s["dWo"], s["dX"],
+                                       b, sq, hl, kv, dh, causal=True, ws=s["bws"])
+
     # ---- grouped-query attention shard: b 4, s 2048, h 4096, 32 query / 8
     #      kv heads of 128 over 4 shards -> 8 query + 2 kv heads per shard
     def gqa(self):
@@ -364,6 +393,15 @@ def rows(torch, tp, steps, warmup):
                               "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
                               "note": "8 query + 2 kv heads: QKV GEMM + causal attention + W_o GEMM"}
     del s
+    for key, kvl in (("mha_heads_shard_backward", None), ("gqa_heads_shard_backward", 2)):
+        s = R.mha_bwd(kvl)
+        gbw = graph_of(torch, lambda: R.attn_bwd(s))
+        ms_bw, _ = timed(torch, lambda kt: gbw.replay(), s_ms, w_ms)
+        fb = s["flop_bwd_gemm"] + s["flop_bwd_att"]
+        out[key] = {"ms": ms_bw, "tflops": fb / ms_bw / 1e9, "frac_peak": fb / ms_bw / 1e9 / PEAK_BF16_TFLOPS,
+                    "note": "dO, dWo, dWqkv, dX GEMMs + attention backward counted as 2.5x the causal "
+                            "forward (S recompute, dP, dV, dK, dQ); the kernels recompute S and dP twice"}
+        del s
     s = R.sp_ln()
     gl = graph_of(torch, lambda: R.sp_ln_step(s))
     ms_l, _ = timed(torch, lambda kt: gl.replay(), s_ms, w_ms)
@@ -419,6 +457,9 @@ def run_op(torch, tp, synth, name, iters):
         elif name == "c6_gqa":
             s = R.gqa()
             fn = lambda: R.gqa_attn(s)
+        elif name in ("c9_attn_bwd", "c10_gqa_bwd"):
+            s = R.mha_bwd(None if name == "c9_attn_bwd" else 2)
+            fn = lambda: R.attn_bwd(s)
         elif name == "c7_spln":
             s = R.sp_ln()
             fn = lambda: R.sp_ln_step(s)

@@ -193,7 +193,9 @@ size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t head
  *   Outputs (float32, dense unless noted): dWqkv [h x (hl + 2*kvl)*d],
  *        dWo [hl*d x h], dXi [b*s x h] with row stride lddx.
  *   ws   tp_attn_shard_backward_workspace() bytes: dO_i (bf16), D (fp32),
- *        [dQ | dK | dV] (bf16, packed like QKV_i).
+ *        [dQ | dK | dV] (bf16, packed like QKV_i) and, for grouped-query
+ *        shards whose kv heads alone would not fill the device, fp32 dK/dV
+ *        partials of head subsets (added in a fixed order).
  * bf16 and d == 128 only; shape rules as for tp_attn_gqa_shard.  Both
  * workspaces 256-byte aligned.  Every sum runs in a fixed order: repeated
  * calls give identical bits.

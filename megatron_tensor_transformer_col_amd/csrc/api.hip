@@ -142,7 +142,7 @@ AttnWs attn_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
 // backward workspace: dO_i (bf16 [T x hl*d]), D (fp32 [b][hl][s]) and
 // dQKV_i (bf16, packed like QKV_i)
 struct AttnBwdWs {
-  size_t dO, D, dqkv, total;
+  size_t dO, D, dqkv, part, total;
 };
 AttnBwdWs attn_bwd_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
   const size_t T = (size_t)b * (size_t)s;
@@ -150,7 +150,8 @@ AttnBwdWs attn_bwd_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) 
   w.dO = 0;
   w.D = round256(T * (size_t)hl * (size_t)d * 2);
   w.dqkv = w.D + round256(T * (size_t)hl * 4);
-  w.total = w.dqkv + round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
+  w.part = w.dqkv + round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
+  w.total = w.part + round256(attn_bwd_part_bytes(b, s, hl, kvl));
   return w;
 }
 
@@ -261,6 +262,7 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
   void *dO = base + L.dO;
   float *Dr = reinterpret_cast<float *>(base + L.D);
   void *dqkv = base + L.dqkv;
+  float *part = L.total > L.part ? reinterpret_cast<float *>(base + L.part) : nullptr;
 
   if (T > 0) {
     // dO_i = dY Wo_i^T  (row-parallel output projection, input gradient)
@@ -283,7 +285,7 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
     TRY(hip_status(launch_gemm(g, st), "dWo GEMM"));
   }
   if (T > 0)
-    TRY(hip_status(launch_attn_bwd(qkv, wqkv, O, w, lse, dO, w, Dr, dqkv, b, s_len, heads_local,
+    TRY(hip_status(launch_attn_bwd(qkv, wqkv, O, w, lse, dO, w, Dr, dqkv, part, b, s_len, heads_local,
                                    kv_heads_local, d, causal != 0, st),
                    "attention backward"));
   // dWqkv_i = X^T dQKV_i  (column-parallel weight gradient)

@@ -64,6 +64,9 @@ struct BwArgs {
   uint16_t *dqkv;       // gradients, same packing and stride as qkv
   int64_t lddq;
   int s, hl, kvl, group, nbh, nblk;
+  int64_t T;            // b * s
+  int hsplit;           // dK/dV: workgroups sharing one kv head's query heads
+  float *part;          // hsplit > 1: fp32 dK/dV partials [hsplit][b*s][kvl][2][d]
   float scale_log2;     // log2(e) / sqrt(d)
   float scale;          // 1 / sqrt(d)
 };
@@ -169,9 +172,10 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
   dma.init(wave, lane);
   const uint32_t lds0 = lds_addr(smem);
 
-  int rank, bh;
-  bw_place(a, rank, bh);
+  int rank, bhs;
+  bw_place(a, rank, bhs);
   const int kb = rank;  // key block 0 (longest under a causal mask) first
+  const int hs = bhs % a.hsplit, bh = bhs / a.hsplit;
   const int bi = bh / a.kvl, kvh = bh % a.kvl;
   const int64_t tok0 = (int64_t)bi * a.s;
   const int key0 = kb * BW_BLK;
@@ -207,7 +211,8 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
   const int qt0 = CAUSAL ? key0 / BW_TROWS : 0;
   const float c = a.scale_log2;
 
-  for (int hg = 0; hg < a.group; ++hg) {
+  const int hper = a.group / a.hsplit;  // query heads of this workgroup
+  for (int hg = hs * hper; hg < (hs + 1) * hper; ++hg) {
     const int head = kvh * a.group + hg;
     const uint16_t *Qg = a.qkv + tok0 * a.ldq + head * BW_D;
     const uint16_t *dOg = a.dO + tok0 * a.lddo + head * BW_D;
@@ -303,6 +308,20 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
   }
 
   // lane holds dK^T / dV^T rows d = dt*16 + 4g + r of key k_w + kt*16 + l16
+  if (a.hsplit > 1) {  // fp32 partial of this head subset; attn_bwd_kv_sum_kernel adds them
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int key = k_w + kt * 16 + l16;
+      if (key >= a.s) continue;
+      float *pr = a.part + (((int64_t)hs * a.T + tok0 + key) * a.kvl + kvh) * 2 * BW_D;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        *reinterpret_cast<f32x4_t *>(pr + dt * 16 + 4 * g) = dk[dt][kt] * a.scale;
+        *reinterpret_cast<f32x4_t *>(pr + BW_D + dt * 16 + 4 * g) = dv[dt][kt];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
     const int key = k_w + kt * 16 + l16;
@@ -456,8 +475,45 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dq_kernel(BwArgs a) {
   }
 }
 
+// dK | dV = sum over the hsplit partials in order, rounded to bf16 into the
+// K and V blocks of dqkv; one thread per 4 consecutive elements of a row
+__global__ void __launch_bounds__(256) attn_bwd_kv_sum_kernel(const float *__restrict__ part, int hsplit, int64_t T,
+                                                              int hl, int kvl, uint16_t *dqkv, int64_t lddq) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (token, kv head, K|V, d/4)
+  const int64_t per_tok = (int64_t)kvl * 2 * (BW_D / 4);
+  if (i >= T * per_tok) return;
+  const int64_t tok = i / per_tok;
+  const int rem = (int)(i % per_tok);
+  const int kvh = rem / (2 * (BW_D / 4));
+  const int w = (rem / (BW_D / 4)) & 1;
+  const int d4 = rem % (BW_D / 4);
+  const int64_t src = ((tok * kvl + kvh) * 2 + w) * BW_D + d4 * 4;
+  f32x4_t acc = *reinterpret_cast<const f32x4_t *>(part + src);
+  for (int hs = 1; hs < hsplit; ++hs) acc += *reinterpret_cast<const f32x4_t *>(part + hs * T * kvl * 2 * BW_D + src);
+  *reinterpret_cast<uint2 *>(dqkv + tok * lddq + (hl + w * kvl + kvh) * BW_D + d4 * 4) =
+      make_uint2(pack_bf2(acc[0], acc[1]), pack_bf2(acc[2], acc[3]));
+}
+
+// Workgroups that share one kv head's query heads in the dK/dV pass: with
+// fewer than 512 (sequence, kv head, key block) workgroups the group's heads
+// are split (a power of two dividing the group) so the chip fills; each
+// split writes an fp32 partial that attn_bwd_kv_sum_kernel adds in order.
+int attn_bwd_hsplit(int64_t b, int64_t s, int64_t heads_local, int64_t kv_heads_local) {
+  if (kv_heads_local < 1 || heads_local % kv_heads_local) return 1;
+  const int64_t g = heads_local / kv_heads_local;
+  const int64_t wgs = b * kv_heads_local * ((s + BW_BLK - 1) / BW_BLK);
+  int64_t hs = 1;
+  while (hs < g && g % (2 * hs) == 0 && wgs * hs < 512) hs *= 2;
+  return (int)hs;
+}
+
+size_t attn_bwd_part_bytes(int64_t b, int64_t s, int64_t heads_local, int64_t kv_heads_local) {
+  const int hs = attn_bwd_hsplit(b, s, heads_local, kv_heads_local);
+  return hs > 1 ? (size_t)hs * (size_t)(b * s) * (size_t)kv_heads_local * 2 * BW_D * 4 : 0;
+}
+
 hipError_t launch_attn_bwd(const void *qkv, int64_t ldqkv, const void *O, int64_t ldo, const float *lse,
-                           const void *dO, int64_t lddo, float *Dr, void *dqkv, int64_t b, int64_t s,
+                           const void *dO, int64_t lddo, float *Dr, void *dqkv, float *part, int64_t b, int64_t s,
                            int64_t heads_local, int64_t kv_heads_local, int64_t d, bool causal, hipStream_t st) {
   if (b <= 0 || s <= 0 || heads_local <= 0) return hipSuccess;
   if (d != BW_D) return hipErrorInvalidValue;
@@ -485,12 +541,22 @@ hipError_t launch_attn_bwd(const void *qkv, int64_t ldqkv, const void *O, int64_
   a.scale_log2 = 1.4426950408889634f / sqrtf((float)d);
   a.nblk = (int)((s + BW_BLK - 1) / BW_BLK);
 
-  a.nbh = (int)(b * kv_heads_local);
+  a.T = T;
+  a.hsplit = attn_bwd_hsplit(b, s, heads_local, kv_heads_local);
+  a.part = part;
+  if (a.hsplit > 1 && part == nullptr) return hipErrorInvalidValue;
+  a.nbh = (int)(b * kv_heads_local * a.hsplit);
   const dim3 g1((unsigned)(a.nbh * a.nblk));
   if (causal)
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, g1, dim3(BW_NW * 64), 0, st, a);
   else
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, g1, dim3(BW_NW * 64), 0, st, a);
+  if (a.hsplit > 1) {
+    const int64_t n4 = T * kv_heads_local * 2 * (BW_D / 4);
+    hipLaunchKernelGGL(attn_bwd_kv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, a.hsplit,
+                       T, (int)heads_local, (int)kv_heads_local, a.dqkv, a.lddq);
+  }
+  a.hsplit = 1;
   a.nbh = (int)(b * heads_local);
   const dim3 g2((unsigned)(a.nbh * a.nblk));
   if (causal)

@@ -72,9 +72,12 @@ hipError_t launch_flash_attn(const void *qkv, int64_t ldqkv, void *O, int64_t ld
 // Attention backward from the forward's packed QKV, O and lse: D (fp32
 // [b][heads_local][s], written) then dQ | dK | dV into dqkv (bf16, same
 // packing and stride as qkv)
+// (part: attn_bwd_part_bytes() of fp32 scratch for the split dK/dV partials,
+// NULL allowed when that is 0)
 hipError_t launch_attn_bwd(const void *qkv, int64_t ldqkv, const void *O, int64_t ldo, const float *lse,
-                           const void *dO, int64_t lddo, float *Dr, void *dqkv, int64_t b, int64_t s,
+                           const void *dO, int64_t lddo, float *Dr, void *dqkv, float *part, int64_t b, int64_t s,
                            int64_t heads_local, int64_t kv_heads_local, int64_t d, bool causal, hipStream_t st);
+size_t attn_bwd_part_bytes(int64_t b, int64_t s, int64_t heads_local, int64_t kv_heads_local);
 
 // db[n] = sum_m dZ[m][n] (dZ dtype, db float32).
 hipError_t launch_rs_layernorm(int out_dtype, int64_t rows, int64_t N, int n, const float *const *parts,

@@ -62,8 +62,12 @@ def test_workspace_sizes():
     T = 4 * 2048
     assert tp.tp_attn_heads_shard_workspace(1, 4, 2048, 8, 128) == T * 3 * 1024 * 2 + T * 1024 * 2 + T * 8 * 4
     assert tp.tp_attn_gqa_shard_workspace(1, 4, 2048, 8, 2, 128) == T * 12 * 128 * 2 + T * 1024 * 2 + T * 8 * 4
-    # attention backward: dO [T x hl d] bf16 + D [b hl s] fp32 + dQKV bf16
-    assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 128) == T * 1024 * 2 + T * 8 * 4 + T * 12 * 128 * 2
+    # attention backward: dO [T x hl d] bf16 + D [b hl s] fp32 + dQKV bf16, plus for
+    # grouped-query shards with few (sequence, kv head, 128-key block) pairs the
+    # fp32 dK/dV partials of the 4 head splits [4][T][kvl][2][d]
+    assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 8, 128) == T * 1024 * 2 + T * 8 * 4 + T * 24 * 128 * 2
+    assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 128) == (
+        T * 1024 * 2 + T * 8 * 4 + T * 12 * 128 * 2 + 4 * T * 2 * 2 * 128 * 4)
     # backward: dH, H, dZ (GELU) / dH, H, [dZg | dZu] (SwiGLU)
     assert tp.tp_mlp_shard_backward_workspace(1, 1, 8192, 1024) == 3 * 8192 * 1024 * 2
     assert tp.tp_mlp_shard_backward_workspace(1, 2, 8192, 3584) == 4 * 8192 * 3584 * 2
