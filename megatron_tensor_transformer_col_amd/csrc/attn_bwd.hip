@@ -35,11 +35,14 @@
 //  HBM or accumulating dQ with atomics: the sums stay in a fixed order.
 //
 // LDS tiles are [row][128] bf16 rows of 256 bytes (16 granules of 16 B);
-// granule c of row r is stored at c ^ f(r & 15), f(r) = 2 (r & 7) + (r >> 3).
-// Sixteen consecutive rows read at one logical granule (ds_read_b128) hit 16
-// different slots, and the transpose reads (rows 4g + e, granule pairs)
-// cover all slots of a 256-byte bank cycle, so both access patterns are
-// conflict free on one layout.
+// granule c of row r is stored at c ^ f(r & 15), f a bit-linear permutation
+// of 0..15: f(r) = 2 (r & 7) ^ ((r >> 2) & 1) ^ (r & 8).  Both reads of a
+// tile are then conflict free -- the 16-byte row reads (16 consecutive rows
+// at one logical granule; every 8 lanes on distinct banks too) and the
+// transpose reads (rows 4g + e, pairs of granules) -- which a brute-force
+// check over the lane patterns confirms for both plausible bank models.  (A
+// simpler f = 2 (r & 7) + (r >> 3) measured two conflict cycles per LDS
+// instruction: its 8-lane groups of row reads collide.)
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "lds_dma.hpp"
@@ -55,7 +58,7 @@ static constexpr int BW_BLK = BW_NW * BW_WROWS;   // keys / queries per workgrou
 static constexpr int BW_JN = BW_TROWS / (4 * BW_NW);  // wave-DMAs per wave per tile
 static constexpr int64_t BW_MAX_LD = int64_t(1) << 24;
 
-__device__ __forceinline__ int bw_swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int bw_swz(int r) { return ((r & 7) << 1) ^ ((r >> 2) & 1) ^ (r & 8); }
 
 struct BwArgs {
   const uint16_t *qkv;  // forward's packed [Q (hl heads) | K (kvl) | V (kvl)], token-major
@@ -238,6 +241,9 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
       if (CAUSAL && q0 + BW_TROWS - 1 < k_w) continue;  // every query precedes this wave's keys
       const uint16_t *Qs = smem + st * 2 * BW_TILE;
       const uint16_t *dOs = Qs + BW_TILE;
+      const bool full = q0 + BW_TROWS <= a.s;
+      const bool edge = !full || (CAUSAL && q0 < k_w + BW_WROWS - 1);
+      const bool vec4 = full && (a.s & 3) == 0;  // lse / D rows 16-byte aligned
 
       // two halves of 32 queries: kc selects query tiles 2kc, 2kc+1
 #pragma unroll
@@ -264,29 +270,50 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
             }
           }
         }
-        // P and dS; lane holds queries q0 + (2kc+h2)*16 + 4g + r of key k_w + kt*16 + l16
+        // P and dS; lane holds queries q0 + (2kc+h2)*16 + 4g + r of key k_w + kt*16 + l16.
+        // Only tiles that cross the diagonal or the end of the sequence need the
+        // mask (keys past the end are discarded at the store; queries past it
+        // must not contribute); the test is wave-uniform.
         uint4 pf[2], sf[2];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int qb = q0 + (2 * kc + h2) * 16 + 4 * g;
           float lq[4], dq[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = min(qb + r, a.s - 1);
-            lq[r] = lse[q];
-            dq[r] = Dr[q];
-          }
-#pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
-            const int key = k_w + kt * 16 + l16;
+          if (vec4) {
+            const float4 l4 = *reinterpret_cast<const float4 *>(lse + qb);
+            const float4 d4 = *reinterpret_cast<const float4 *>(Dr + qb);
+            lq[0] = l4.x; lq[1] = l4.y; lq[2] = l4.z; lq[3] = l4.w;
+            dq[0] = d4.x; dq[1] = d4.y; dq[2] = d4.z; dq[3] = d4.w;
+          } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              const int q = qb + r;
-              const bool ok = q < a.s && (!CAUSAL || key <= q);
-              const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[h2][kt][r], c, -lq[r])) : 0.f;
-              S[h2][kt][r] = p;
-              dP[h2][kt][r] = p * (dP[h2][kt][r] - dq[r]);
+              const int q = min(qb + r, a.s - 1);
+              lq[r] = lse[q];
+              dq[r] = Dr[q];
             }
+          }
+          if (edge) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const int key = k_w + kt * 16 + l16;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int q = qb + r;
+                const bool ok = q < a.s && (!CAUSAL || key <= q);
+                const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[h2][kt][r], c, -lq[r])) : 0.f;
+                S[h2][kt][r] = p;
+                dP[h2][kt][r] = p * (dP[h2][kt][r] - dq[r]);
+              }
+            }
+          } else {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(S[h2][kt][r], c, -lq[r]));
+                S[h2][kt][r] = p;
+                dP[h2][kt][r] = p * (dP[h2][kt][r] - dq[r]);
+              }
           }
         }
 #pragma unroll
