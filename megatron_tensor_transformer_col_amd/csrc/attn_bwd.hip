@@ -465,17 +465,21 @@ __global__ void __launch_bounds__(BW_NW * 64, 2) attn_bwd_dq_kernel(BwArgs a) {
           }
         }
       }
-      // dS^T: lane holds keys k0 + (2kc+h2)*16 + 4g + r of query q_w + qt*16 + l16
+      // dS^T: lane holds keys k0 + (2kc+h2)*16 + 4g + r of query q_w + qt*16 + l16.
+      // A key is visible when its offset (2kc+h2)*16 + r from the lane's first
+      // key k0 + 4g is at most kmax: before the end of the sequence and, with
+      // the causal mask, at or below the query.  Queries past the end only
+      // feed their own, unstored dQ rows.
       uint4 sf[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const int q = q_w + qt * 16 + l16;
+        const int kmax = (CAUSAL ? min(q, a.s - 1) : a.s - 1) - (k0 + 4 * g);
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int key = k0 + (2 * kc + h2) * 16 + 4 * g + r;
-            const bool ok = key < a.s && q < a.s && (!CAUSAL || key <= q);
+            const bool ok = (2 * kc + h2) * 16 + r <= kmax;
             const float p = ok ? __builtin_amdgcn_exp2f(fmaf(S[h2][qt][r], c, -lq[qt])) : 0.f;
             dP[h2][qt][r] = p * (dP[h2][qt][r] - dq[qt]);
           }
