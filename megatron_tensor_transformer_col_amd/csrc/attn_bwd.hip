@@ -15,10 +15,12 @@
 // Three kernels, none of which waits on another workgroup, all bitwise
 // repeatable:
 //  * attn_bwd_dot_kernel: D for every (token, head).
-//  * attn_bwd_dkdv_kernel: a workgroup owns 128 keys of one (sequence, kv
-//    head), 32 per wave, and keeps K, V (as MFMA B operands) and the fp32
-//    dK^T, dV^T accumulators in registers while 64-query tiles of Q and dO
-//    stream through LDS by direct DMA (two stages).  Per tile:
+//  * attn_bwd_dkdv_kernel: a workgroup of 8 waves owns 128 keys of one
+//    (sequence, kv head), 16 per wave (two waves per SIMD; 32 keys per wave
+//    need ~360 VGPRs and measured 7% slower at one wave per SIMD), and keeps
+//    K, V (as MFMA B operands) and the fp32 dK^T, dV^T accumulators in
+//    registers while 64-query tiles of Q and dO, with the tile's lse2 and D
+//    rows, stream through LDS by direct DMA (two stages).  Per tile:
 //    S = Q K^T and dP = dO V^T (Q / dO fragments by ds_read_b128), then
 //    P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS with the
 //    dO^T / Q^T operands from ds_read_b64_tr_b16 transpose reads.  The
@@ -55,7 +57,8 @@ static constexpr int BW_TILE = BW_TROWS * BW_D;   // elements of one tile (16 Ki
 static constexpr int BW_NW = 4;                   // waves per workgroup
 static constexpr int BW_WROWS = 32;               // keys (dK/dV) or queries (dQ) per wave
 static constexpr int BW_BLK = BW_NW * BW_WROWS;   // keys / queries per workgroup
-static constexpr int BW_JN = BW_TROWS / (4 * BW_NW);  // wave-DMAs per wave per tile
+static constexpr int DK_NW = 8;                   // dK/dV: waves per workgroup ...
+static constexpr int DK_KT = 1;                   // ... of 16 * DK_KT keys each
 static constexpr int64_t BW_MAX_LD = int64_t(1) << 24;
 
 __device__ __forceinline__ int bw_swz(int r) { return ((r & 7) << 1) ^ ((r >> 2) & 1) ^ (r & 8); }
@@ -77,10 +80,13 @@ struct BwArgs {
   float scale;          // 1 / sqrt(d)
 };
 
-// Per-lane DMA slot of a 4-wave tile copy: lane i of wave w fetches row
-// 4w + i/16 (+16 per further wave-DMA) and the global granule that lands
-// in LDS slot i % 16 of that row.
+// Per-lane DMA slot of an NW-wave tile copy: lane i of wave w fetches row
+// 4w + i/16 (+4 NW per further wave-DMA, a multiple of 16, so the row's
+// swizzle stays the lane's) and the global granule that lands in LDS slot
+// i % 16 of that row.
+template <int NW>
 struct BwDma {
+  static constexpr int JN = BW_TROWS / (4 * NW);  // wave-DMAs per wave per tile
   int row_lo;
   uint32_t gran;  // byte offset of the fetched granule within its row
   __device__ __forceinline__ void init(int wave, int lane) {
@@ -95,14 +101,14 @@ struct BwDma {
     const uint32_t ldb = (uint32_t)ld * 2u;
     if (r0 + BW_TROWS <= limit) {
 #pragma unroll
-      for (int j = 0; j < BW_JN; ++j)
-        dma16s((uint32_t)row_lo * ldb + gran, G + (int64_t)(r0 + 16 * j) * ld, dst + (wave + BW_NW * j) * 1024);
+      for (int j = 0; j < JN; ++j)
+        dma16s((uint32_t)row_lo * ldb + gran, G + (int64_t)(r0 + 4 * NW * j) * ld, dst + (wave + NW * j) * 1024);
     } else {
       const uint16_t *base = G + (int64_t)r0 * ld;
 #pragma unroll
-      for (int j = 0; j < BW_JN; ++j) {
-        const uint32_t r = (uint32_t)min(16 * j + row_lo, limit - 1 - r0);
-        dma16s(r * ldb + gran, base, dst + (wave + BW_NW * j) * 1024);
+      for (int j = 0; j < JN; ++j) {
+        const uint32_t r = (uint32_t)min(4 * NW * j + row_lo, limit - 1 - r0);
+        dma16s(r * ldb + gran, base, dst + (wave + NW * j) * 1024);
       }
     }
   }
@@ -168,13 +174,17 @@ __global__ void __launch_bounds__(256) attn_bwd_dot_kernel(const uint16_t *__res
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <bool CAUSAL>
-__global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * BW_TILE];  // 2 stages x (Q, dO)
+// NW waves of 16*KT keys each, NW * 16 * KT == BW_BLK keys per workgroup
+template <bool CAUSAL, int NW, int KT>
+__global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(BwArgs a) {
+  static_assert(NW * 16 * KT == BW_BLK, "keys per workgroup");
+  // 2 stages x (Q tile, dO tile, the tile's lse2 and D rows: 1 KiB)
+  constexpr int STG = 2 * BW_TILE + 512;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * STG];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  BwDma dma;
+  BwDma<NW> dma;
   dma.init(wave, lane);
   const uint32_t lds0 = lds_addr(smem);
 
@@ -185,14 +195,14 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
   const int bi = bh / a.kvl, kvh = bh % a.kvl;
   const int64_t tok0 = (int64_t)bi * a.s;
   const int key0 = kb * BW_BLK;
-  const int k_w = key0 + wave * BW_WROWS;
+  const int k_w = key0 + wave * 16 * KT;
 
-  // K, V of this wave's 32 keys as B operands: lane supplies row key, d = dc*32 + g*8 ..
+  // K, V of this wave's keys as B operands: lane supplies row key, d = dc*32 + g*8 ..
   const uint16_t *Kg = a.qkv + tok0 * a.ldq + (a.hl + kvh) * BW_D;
   const uint16_t *Vg = a.qkv + tok0 * a.ldq + (a.hl + a.kvl + kvh) * BW_D;
-  uint4 kf[2][4], vf[2][4];
+  uint4 kf[KT][4], vf[KT][4];
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = k_w + kt * 16 + l16;
 #pragma unroll
     for (int dc = 0; dc < 4; ++dc) {
@@ -204,11 +214,11 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
       }
     }
   }
-  f32x4_t dk[8][2], dv[8][2];
+  f32x4_t dk[8][KT], dv[8][KT];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       dk[dt][kt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
       dv[dt][kt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
     }
@@ -225,34 +235,39 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
     const float *lse = a.lse + ((int64_t)bi * a.hl + head) * a.s;
     const float *Dr = a.Dr + ((int64_t)bi * a.hl + head) * a.s;
 
+    // Tiles whose 64 rows all exist, with 16-byte aligned rows of lse2 / D
+    // (s % 4 == 0), also bring those rows into LDS (wave 0: lanes 0..15 lse2,
+    // 16..31 D, 32..63 the same again); other tiles read them from memory.
+    auto issue = [&](int jt, uint32_t dst) {
+      dma.tile(Qg, a.ldq, jt * BW_TROWS, a.s, dst, wave);
+      dma.tile(dOg, a.lddo, jt * BW_TROWS, a.s, dst + BW_TILE * 2, wave);
+      if (wave == 0 && jt * BW_TROWS + BW_TROWS <= a.s && (a.s & 3) == 0)
+        dma16(reinterpret_cast<const uint16_t *>(((lane & 16) ? Dr : lse) + jt * BW_TROWS + 4 * (lane & 15)),
+              dst + 4 * BW_TILE);
+    };
     __syncthreads();  // the previous head's readers are done with both stages
-    dma.tile(Qg, a.ldq, qt0 * BW_TROWS, a.s, lds0, wave);
-    dma.tile(dOg, a.lddo, qt0 * BW_TROWS, a.s, lds0 + BW_TILE * 2, wave);
+    issue(qt0, lds0);
     for (int j = qt0; j < nqt; ++j) {
       wait_vmcnt<0>();
       __syncthreads();  // tile j landed for every wave; the other stage is free
       const int st = (j - qt0) & 1;
-      if (j + 1 < nqt) {
-        const uint32_t dst = lds0 + (uint32_t)((st ^ 1) * 2 * BW_TILE * 2);
-        dma.tile(Qg, a.ldq, (j + 1) * BW_TROWS, a.s, dst, wave);
-        dma.tile(dOg, a.lddo, (j + 1) * BW_TROWS, a.s, dst + BW_TILE * 2, wave);
-      }
+      if (j + 1 < nqt) issue(j + 1, lds0 + (uint32_t)((st ^ 1) * STG * 2));
       const int q0 = j * BW_TROWS;
       if (CAUSAL && q0 + BW_TROWS - 1 < k_w) continue;  // every query precedes this wave's keys
-      const uint16_t *Qs = smem + st * 2 * BW_TILE;
+      const uint16_t *Qs = smem + st * STG;
       const uint16_t *dOs = Qs + BW_TILE;
-      const bool full = q0 + BW_TROWS <= a.s;
-      const bool edge = !full || (CAUSAL && q0 < k_w + BW_WROWS - 1);
-      const bool vec4 = full && (a.s & 3) == 0;  // lse / D rows 16-byte aligned
+      const float *stats = reinterpret_cast<const float *>(Qs + 2 * BW_TILE);  // lse2 [64], D [64]
+      const bool staged = q0 + BW_TROWS <= a.s && (a.s & 3) == 0;
+      const bool edge = q0 + BW_TROWS > a.s || (CAUSAL && q0 < k_w + 16 * KT - 1);
 
       // two halves of 32 queries: kc selects query tiles 2kc, 2kc+1
 #pragma unroll
       for (int kc = 0; kc < 2; ++kc) {
-        f32x4_t S[2][2], dP[2][2];
+        f32x4_t S[2][KT], dP[2][KT];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < KT; ++kt) {
             S[h2][kt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
             dP[h2][kt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
           }
@@ -264,7 +279,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
             const uint4 qa = lds_frag(Qs, row, dc * 4 + g);
             const uint4 da = lds_frag(dOs, row, dc * 4 + g);
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < KT; ++kt) {
               S[h2][kt] = mfma16(qa, kf[kt][dc], S[h2][kt]);
               dP[h2][kt] = mfma16(da, vf[kt][dc], dP[h2][kt]);
             }
@@ -274,16 +289,19 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
         // Only tiles that cross the diagonal or the end of the sequence need the
         // mask (keys past the end are discarded at the store; queries past it
         // must not contribute); the test is wave-uniform.
-        uint4 pf[2], sf[2];
+        uint4 pf[KT], sf[KT];
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2) {
           const int qb = q0 + (2 * kc + h2) * 16 + 4 * g;
           float lq[4], dq[4];
-          if (vec4) {
-            const float4 l4 = *reinterpret_cast<const float4 *>(lse + qb);
-            const float4 d4 = *reinterpret_cast<const float4 *>(Dr + qb);
-            lq[0] = l4.x; lq[1] = l4.y; lq[2] = l4.z; lq[3] = l4.w;
-            dq[0] = d4.x; dq[1] = d4.y; dq[2] = d4.z; dq[3] = d4.w;
+          if (staged) {
+            const f32x4_t l4 = *reinterpret_cast<const f32x4_t *>(stats + qb - q0);
+            const f32x4_t d4 = *reinterpret_cast<const f32x4_t *>(stats + BW_TROWS + qb - q0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              lq[r] = l4[r];
+              dq[r] = d4[r];
+            }
           } else {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -294,7 +312,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
           }
           if (edge) {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < KT; ++kt) {
               const int key = k_w + kt * 16 + l16;
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
@@ -307,7 +325,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
             }
           } else {
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+            for (int kt = 0; kt < KT; ++kt)
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
                 const float p = __builtin_amdgcn_exp2f(fmaf(S[h2][kt][r], c, -lq[r]));
@@ -317,7 +335,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
           }
         }
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < KT; ++kt) {
           pf[kt] = pack8(S[0][kt], S[1][kt]);
           sf[kt] = pack8(dP[0][kt], dP[1][kt]);
         }
@@ -327,7 +345,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
           const uint4 ot = lds_trans(dOs, kc, dt, g, l16);
           const uint4 qt = lds_trans(Qs, kc, dt, g, l16);
 #pragma unroll
-          for (int kt = 0; kt < 2; ++kt) {
+          for (int kt = 0; kt < KT; ++kt) {
             dv[dt][kt] = mfma16(ot, pf[kt], dv[dt][kt]);
             dk[dt][kt] = mfma16(qt, sf[kt], dk[dt][kt]);
           }
@@ -340,7 +358,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
   // lane holds dK^T / dV^T rows d = dt*16 + 4g + r of key k_w + kt*16 + l16
   if (a.hsplit > 1) {  // fp32 partial of this head subset; attn_bwd_kv_sum_kernel adds them
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       const int key = k_w + kt * 16 + l16;
       if (key >= a.s) continue;
       float *pr = a.part + (((int64_t)hs * a.T + tok0 + key) * a.kvl + kvh) * 2 * BW_D;
@@ -353,7 +371,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 1) attn_bwd_dkdv_kernel(BwArgs a) 
     return;
   }
 #pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
+  for (int kt = 0; kt < KT; ++kt) {
     const int key = k_w + kt * 16 + l16;
     if (key >= a.s) continue;
     uint16_t *dKr = a.dqkv + (tok0 + key) * a.lddq + (a.hl + kvh) * BW_D;
@@ -375,7 +393,7 @@ __global__ void __launch_bounds__(BW_NW * 64, 2) attn_bwd_dq_kernel(BwArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  BwDma dma;
+  BwDma<BW_NW> dma;
   dma.init(wave, lane);
   const uint32_t lds0 = lds_addr(smem);
 
@@ -582,9 +600,9 @@ hipError_t launch_attn_bwd(const void *qkv, int64_t ldqkv, const void *O, int64_
   a.nbh = (int)(b * kv_heads_local * a.hsplit);
   const dim3 g1((unsigned)(a.nbh * a.nblk));
   if (causal)
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<true>, g1, dim3(BW_NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<true, DK_NW, DK_KT>), g1, dim3(DK_NW * 64), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_bwd_dkdv_kernel<false>, g1, dim3(BW_NW * 64), 0, st, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<false, DK_NW, DK_KT>), g1, dim3(DK_NW * 64), 0, st, a);
   if (a.hsplit > 1) {
     const int64_t n4 = T * kv_heads_local * 2 * (BW_D / 4);
     hipLaunchKernelGGL(attn_bwd_kv_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, a.hsplit,
