@@ -140,7 +140,11 @@ def _mat(t, name):
     """(pointer, rows, cols, ld) of a 2-D row-major tensor (or None)."""
     if t is None:
         return None, 0, 0, 0
-    if t.dim() != 2 or (t.size(1) > 1 and t.stride(1) != 1):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D row-major tensor view")
+    if t.numel() == 0:  # no element is read: any strides, row stride = width
+        return t.data_ptr(), t.size(0), t.size(1), max(t.size(1), 1)
+    if t.size(1) > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} must be a 2-D row-major tensor view")
     return t.data_ptr(), t.size(0), t.size(1), t.stride(0)
 

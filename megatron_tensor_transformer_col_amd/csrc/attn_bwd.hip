@@ -31,8 +31,7 @@
 //    stream through LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T, then
 //    dS^T, then dQ^T += K^T dS^T (K^T by transpose reads).  It fits in 256
 //    VGPRs, so two workgroups share a CU (two waves per SIMD; 25% faster
-//    than one).  The dK/dV kernel needs ~360 (its fp32 dK^T, dV^T
-//    accumulators alone take 128) and runs one wave per SIMD.
+//    than one).
 //  S and dP are recomputed in both kernels rather than exchanging dS through
 //  HBM or accumulating dQ with atomics: the sums stay in a fixed order.
 //
@@ -54,9 +53,9 @@ namespace tpcol {
 static constexpr int BW_D = 128;
 static constexpr int BW_TROWS = 64;               // rows of one streamed tile
 static constexpr int BW_TILE = BW_TROWS * BW_D;   // elements of one tile (16 KiB)
-static constexpr int BW_NW = 4;                   // waves per workgroup
-static constexpr int BW_WROWS = 32;               // keys (dK/dV) or queries (dQ) per wave
-static constexpr int BW_BLK = BW_NW * BW_WROWS;   // keys / queries per workgroup
+static constexpr int BW_NW = 4;                   // dQ: waves per workgroup ...
+static constexpr int BW_WROWS = 32;               // ... of 32 queries each
+static constexpr int BW_BLK = BW_NW * BW_WROWS;   // keys (dK/dV) / queries (dQ) per workgroup
 static constexpr int DK_NW = 8;                   // dK/dV: waves per workgroup ...
 static constexpr int DK_KT = 1;                   // ... of 16 * DK_KT keys each
 static constexpr int64_t BW_MAX_LD = int64_t(1) << 24;

@@ -165,3 +165,24 @@ def test_full_size_shard_sampled(name):
     rows = slice(bi * W.s, (bi + 1) * W.s)
     ref3 = _shard_oracle(d, hl, kvl, Wqkv, Wo, 1, W.s, True, rows=rows)
     assert_close(host(r["dX"][rows]), ref3["dX"], "bf16", "dX_0 batch element 3")
+
+
+def test_empty_sequence_gives_zero_weight_gradients():
+    """s = 0: nothing to differentiate; the weight gradients are exactly 0
+    (the sum over no tokens) and no kernel reads the (empty) workspaces."""
+    note("attn bwd s=0")
+    T = torch()
+    hl, kvl, h = 2, 1, 256
+    X = T.empty((0, h), dtype=T.bfloat16, device="cuda:0")
+    Wqkv = T.zeros((h, (hl + 2 * kvl) * HD), dtype=T.bfloat16, device="cuda:0")
+    Wo = T.zeros((hl * HD, h), dtype=T.bfloat16, device="cuda:0")
+    P = empty((0, h), "f32")
+    fws = T.empty(max(1, tp.tp_attn_gqa_shard_workspace(tp.TP_BF16, 1, 0, hl, kvl, HD)), dtype=T.uint8,
+                  device="cuda:0")
+    tp.tp_attn_gqa_shard(X, Wqkv, Wo, P, 1, 0, hl, kvl, d=HD, ws=fws)
+    dWqkv = empty((h, (hl + 2 * kvl) * HD), "f32", fill=float("nan"))
+    dWo = empty((hl * HD, h), "f32", fill=float("nan"))
+    dX = empty((0, h), "f32")
+    tp.tp_attn_shard_backward(X, Wqkv, Wo, X, fws, dWqkv, dWo, dX, 1, 0, hl, kvl, d=HD)
+    T.cuda.synchronize()
+    assert T.count_nonzero(dWqkv).item() == 0 and T.count_nonzero(dWo).item() == 0

@@ -103,3 +103,11 @@ def test_rows_of_minus_infinity_and_repeat_is_bitwise():
     assert_close(rows, np.concatenate([masked["rows"], rest["rows"]]), "f32", "row losses")
     for a, b in zip([r1[1], r1[4]] + r1[2] + r1[3], [r2[1], r2[4]] + r2[2] + r2[3]):
         np.testing.assert_array_equal(host(a), host(b))
+
+
+def test_zero_rows():
+    """No token rows: every shard loss and the total are exactly 0."""
+    note("vocab ce T=0")
+    d = synth.make_ce_inputs(0, 64, "bf16", seed=1)
+    stats, lse, losses, rows, total = _run(d, 2, "bf16")
+    assert all(host(x)[0] == 0 for x in losses) and host(total)[0] == 0
