@@ -354,9 +354,17 @@ static hipError_t run_lds(const GemmArgs &a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Tile configurations measured on MI355X (see the design notes): 8 wave64 per
+// Tile configurations measured on MI355X: 8 wave64 per
 // workgroup (two per SIMD, so LDS and DMA latency of one wave hides under
 // the other's MFMAs) and 256-wide tiles to cut L2 -> CU traffic per flop.
+static int64_t cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
 template <int LAYOUT, int EPI, bool DUAL, bool KCAT>
 static hipError_t pick_lds(const GemmArgs &a, hipStream_t s) {
   const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
@@ -365,7 +373,18 @@ static hipError_t pick_lds(const GemmArgs &a, hipStream_t s) {
     if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 2, false>(a, s);
     return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
   } else {
-    if (t256 >= 192) return run_lds<256, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
+    if (t256 >= 192) {
+      // Both large-tile configurations run one workgroup per CU, so a launch
+      // takes ceil(tiles / CUs) rounds; a 256x256 tile costs about 65536 /
+      // 1230 and a 128x256 tile 32768 / 1122 (their measured steady-state
+      // TFLOP/s).  Where 256x256 tiles leave a half-empty last round (e.g.
+      // 8192 x 3072: 384 tiles = 1.5 rounds) the smaller tiles fill theirs.
+      const int64_t cus = cu_count();
+      const double c256 = (double)((t256 + cus - 1) / cus) * (65536.0 / 1230.0);
+      const double c128 = (double)((t128x256 + cus - 1) / cus) * (32768.0 / 1122.0);
+      if (c256 <= c128) return run_lds<256, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
+      return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
+    }
     if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
     return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
   }
