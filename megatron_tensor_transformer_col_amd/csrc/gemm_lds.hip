@@ -158,7 +158,20 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
   constexpr int LOADS = ATile::PER_WAVE + NB * BTile::PER_WAVE;  // DMA ops per wave per slab
   static_assert(STAGES >= 2 && LOADS * (STAGES - 1) < 64, "pipeline depth");
 
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[STAGES * STAGE];
+  // Single-output epilogues write the finished tile through LDS (the ring is
+  // idle by then) when the whole tile fits in 144 KiB: every wave computes
+  // its values at once, then the workgroup stores whole 16-byte chunks of
+  // consecutive rows (the direct stores write 16 rows x 32 or 64 bytes per
+  // instruction, which measured slower).  256 x 256 fp32 tiles (256 KiB)
+  // keep the direct stores: staging them in two row bands idles half the
+  // waves per band and measured slower than storing directly.
+  constexpr int OES = EPI == EPI_STORE_F32 ? 4 : 2;  // output element bytes
+  constexpr int SROW = BN * OES + 16;               // staged row bytes (16-byte pad)
+  constexpr bool STAGED = !DUAL && (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32) &&
+                          BM * SROW <= 144 * 1024;
+  constexpr int RING_EL = STAGES * STAGE;
+  constexpr int STG_EL = STAGED ? BM * SROW / 2 : 0;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[RING_EL > STG_EL ? RING_EL : STG_EL];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -314,6 +327,46 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
   }
 
   // ---- epilogue: lane holds C[row][col .. col+3] of every 16x16 tile
+  if constexpr (STAGED) {
+    using OutT = typename std::conditional<EPI == EPI_STORE_F32, float, uint16_t>::type;
+    char *stg = reinterpret_cast<char *>(smem);
+    constexpr int CPR = BN * OES / 16;  // 16-byte chunks per tile row
+    float bv[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 16 + g * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[j][r] = 0.f;
+      if (p.bias != nullptr && col < N) {
+        if constexpr (EPI == EPI_STORE_F32) load4(static_cast<const float *>(p.bias) + col, bv[j]);
+        else load4(static_cast<const uint16_t *>(p.bias) + col, bv[j]);
+      }
+    }
+    __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][j][r] + bv[j][r];
+          if constexpr (EPI == EPI_GELU) v[r] = gelu_f(v[r]);
+        }
+        char *dst = stg + (wm * WTM + i * 16 + l16) * SROW + (wn * WTN + j * 16 + g * 4) * OES;
+        store4(reinterpret_cast<OutT *>(dst), v);
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+      const int rl = c / CPR, cc = c % CPR;
+      const int row = m0 + rl, col = n0 + cc * (16 / OES);
+      if (row < M && col < N)
+        *reinterpret_cast<uint4 *>(static_cast<OutT *>(p.C) + (int64_t)row * p.ldc + col) =
+            *reinterpret_cast<const uint4 *>(stg + rl * SROW + cc * 16);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i) {
     const int row = m0 + wm * WTM + i * 16 + l16;
