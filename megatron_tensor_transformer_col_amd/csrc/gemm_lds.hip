@@ -167,7 +167,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
   // waves per band and measured slower than storing directly.
   constexpr int OES = EPI == EPI_STORE_F32 ? 4 : 2;  // output element bytes
   constexpr int SROW = BN * OES + 16;               // staged row bytes (16-byte pad)
-  constexpr bool STAGED = !DUAL && (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32) &&
+  constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32 || EPI == EPI_SWIGLU) &&
                           BM * SROW <= 144 * 1024;
   constexpr int RING_EL = STAGES * STAGE;
   constexpr int STG_EL = STAGED ? BM * SROW / 2 : 0;
@@ -352,6 +352,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
         for (int r = 0; r < 4; ++r) {
           v[r] = acc[i][j][r] + bv[j][r];
           if constexpr (EPI == EPI_GELU) v[r] = gelu_f(v[r]);
+          if constexpr (EPI == EPI_SWIGLU) v[r] = silu_f(v[r]) * acc2[DUAL ? i : 0][DUAL ? j : 0][r];
         }
         char *dst = stg + (wm * WTM + i * 16 + l16) * SROW + (wn * WTN + j * 16 + g * 4) * OES;
         store4(reinterpret_cast<OutT *>(dst), v);
