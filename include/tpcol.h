@@ -116,7 +116,7 @@ size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t
  *     P_i = [O_1 ... O_heads_local] @ Wo_i
  * The local heads feed the local row block of Wo directly: no gather of the
  * heads is needed ("Infra: Tensor Parallel", MHA: Wo row-wise, heads
- * column-wise; "张量并行", Multi-Head Attention 的并行化; parallelism survey
+ * column-wise; "张量并行", Multi-Head Attention 的并行化; parallelism overview
  * post, section 1 Tensor Parallelism).  Packing of Wqkv_i columns: Q heads,
  * then K heads, then V heads, head t at offset t*d inside each block
  * ("Megatron-LM 实战 04", TPAttention: qkv reshaped to (3, heads, d)).
@@ -233,7 +233,7 @@ int tp_shard_sum(int out_dtype, int64_t M, int64_t N, int n,
  * Sequence-parallel end of a tensor-parallel block, for one rank: the
  * all-reduce of the row-parallel partials splits into a reduce-scatter and
  * an all-gather, and LayerNorm runs on the rank's reduce-scattered rows
- * (parallelism survey post, 5 Sequence Parallelism).  For the `rows` token
+ * (parallelism overview post, 5 Sequence Parallelism).  For the `rows` token
  * rows of this rank:
  *     Ysum = sum_{i<n} P_i (+ bias, once) (+ residual)
  *     Y    = gamma * (Ysum - mean) / sqrt(var + eps) + beta

@@ -2,7 +2,7 @@
 //
 // In decode every request contributes one token, so a linear layer reads the
 // whole weight once for 2*M*K*N flops: arithmetic intensity is about
-// 2*M / bytes_per_param (parallelism survey post, Prefill-Decode 分离,
+// 2*M / bytes_per_param (parallelism overview post, Prefill-Decode 分离,
 // Decode 阶段), ~16 flop/byte for 16 bf16 tokens, far below the ridge.  The
 // kernel is therefore built for bytes in flight, not for flops:
 //

@@ -3,7 +3,7 @@
 //     Y    = gamma * (Ysum - mean) / sqrt(var + eps) + beta   per row
 // The all-reduce of the row-parallel partials splits into a reduce-scatter
 // (each rank sums its 1/N of the token rows) and an all-gather, and LayerNorm
-// runs on the reduce-scatter's rows (parallelism survey post, 5 Sequence
+// runs on the reduce-scatter's rows (parallelism overview post, 5 Sequence
 // Parallelism).  LayerNorm needs the mean and the population variance of the
 // full hidden row ("张量并行", 相关分析), which each rank has after the
 // reduce-scatter.

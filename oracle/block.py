@@ -46,7 +46,7 @@ def _sigmoid(z):
 
 def silu(z):
     """SiLU(z) = z * sigmoid(z), the gate of the SwiGLU FFN whose W_gate and
-    W_up are column-split (parallelism survey post, section 1 Tensor
+    W_up are column-split (parallelism overview post, section 1 Tensor
     Parallelism); standard definition, not printed on the pages."""
     z = _f64(z)
     return z * _sigmoid(z)
@@ -118,7 +118,7 @@ def mlp_gelu(X, W1, W2, b1=None, b2=None):
 
 def mlp_swiglu(X, Wg, Wu, Wd):
     """Y = (SiLU(X Wg) * (X Wu)) Wd, '*' elementwise.  W_gate and W_up are
-    column-split, the second layer row-split (parallelism survey post,
+    column-split, the second layer row-split (parallelism overview post,
     section 1 Tensor Parallelism)."""
     Zg = linear(X, Wg)
     Zu = linear(X, Wu)
@@ -328,7 +328,7 @@ def layernorm(x, gamma, beta, eps):
 
 
 def reduce_scatter_layernorm(partials, gamma, beta, eps, n, rank, bias=None, residual=None):
-    """Sequence-parallel end of a tensor-parallel block (parallelism survey
+    """Sequence-parallel end of a tensor-parallel block (parallelism overview
     post, 5 Sequence Parallelism: the all-reduce splits into reduce-scatter +
     all-gather, and LayerNorm runs on each shard's 1/N of the tokens).
 
