@@ -169,8 +169,11 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
   constexpr int SROW = BN * OES + 16;               // staged row bytes (16-byte pad)
   constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32 || EPI == EPI_SWIGLU) &&
                           BM * SROW <= 144 * 1024;
+  // The SwiGLU backward (three bf16 outputs, dH read) stages its outputs one
+  // tile at a time the same way.
+  constexpr bool STAGED3 = EPI == EPI_SWIGLU_BWD && 2 * BM * (BN * 2 + 16) <= 144 * 1024;
   constexpr int RING_EL = STAGES * STAGE;
-  constexpr int STG_EL = STAGED ? BM * SROW / 2 : 0;
+  constexpr int STG_EL = STAGED ? BM * SROW / 2 : (STAGED3 ? BM * (BN * 2 + 16) : 0);
   __shared__ __attribute__((aligned(1024))) uint16_t smem[RING_EL > STG_EL ? RING_EL : STG_EL];
 
   const int lane = threadIdx.x & 63;
@@ -365,6 +368,69 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
       if (row < M && col < N)
         *reinterpret_cast<uint4 *>(static_cast<OutT *>(p.C) + (int64_t)row * p.ldc + col) =
             *reinterpret_cast<const uint4 *>(stg + rl * SROW + cc * 16);
+    }
+    return;
+  }
+  if constexpr (STAGED3) {
+    // dH comes into LDS by coalesced 16-byte loads; then each output tile
+    // (dZg, dZu, H) in turn is computed from the accumulators and dH, written
+    // to LDS and stored as whole row chunks.
+    constexpr int SR = BN * 2 + 16;  // staged row bytes
+    constexpr int CPR = BN * 2 / 16;
+    char *dhs = reinterpret_cast<char *>(smem);
+    char *out = dhs + BM * SR;
+    if (p.bias != nullptr) {  // the bias belongs to the gate pre-activation
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + g * 4;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (col < N) load4(static_cast<const uint16_t *>(p.bias) + col, bv);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += bv[r];
+      }
+    }
+    __syncthreads();  // every wave is done reading the ring
+    for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+      const int rl = c / CPR, cc = c % CPR;
+      const int row = m0 + rl, col = n0 + cc * 8;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < M && col < N)
+        v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
+      *reinterpret_cast<uint4 *>(dhs + rl * SR + cc * 16) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int which = 0; which < 3; ++which) {  // 0: dZg, 1: dZu, 2: H
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int off = (wm * WTM + i * 16 + l16) * SR + (wn * WTN + j * 16 + g * 4) * 2;
+          float dh[4], o[4];
+          load4(reinterpret_cast<const uint16_t *>(dhs + off), dh);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float gt = acc[i][j][r], ut = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
+            const float sg = sigmoid_f(gt);
+            const float sl = gt * sg;
+            o[r] = which == 0 ? dh[r] * ut * (sg * (1.0f + gt * (1.0f - sg))) : (which == 1 ? dh[r] * sl : sl * ut);
+          }
+          store4(reinterpret_cast<uint16_t *>(out + off), o);
+        }
+      }
+      __syncthreads();
+      void *C = which == 0 ? p.C : (which == 1 ? p.C3 : p.C2);
+      const int64_t ldc = which == 0 ? p.ldc : (which == 1 ? p.ldc3 : p.ldc2);
+      for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+        const int rl = c / CPR, cc = c % CPR;
+        const int row = m0 + rl, col = n0 + cc * 8;
+        if (row < M && col < N)
+          *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(C) + (int64_t)row * ldc + col) =
+              *reinterpret_cast<const uint4 *>(out + rl * SR + cc * 16);
+      }
+      __syncthreads();
     }
     return;
   }
