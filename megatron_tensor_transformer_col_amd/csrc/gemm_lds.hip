@@ -490,7 +490,10 @@ static hipError_t pick_lds(const GemmArgs &a, hipStream_t s) {
   const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
   const int64_t t128x256 = ((a.M + 127) / 128) * ((a.N + 255) / 256);
   if constexpr (DUAL) {
-    if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 2, false>(a, s);
+    // four 40 KiB stages fill the 160 KiB of LDS (one workgroup per CU
+    // either way: its 8 waves take all the VGPRs); measured 2-8% faster than
+    // two or three stages on the Llama SwiGLU shard
+    if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
     return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
   } else {
     if (t256 >= 192) {

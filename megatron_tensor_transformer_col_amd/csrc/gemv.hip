@@ -12,8 +12,10 @@
 //  * Each ring stage holds a 64-row slab of the strip (8 KiB) and the
 //    matching 16 x 64 slice of x (2 KiB); both move HBM -> LDS with
 //    global_load_lds_dwordx4 (no VGPR staging), three DMA ops per wave per
-//    stage, through a 7-deep ring: six stages (60 KiB) stay in flight per
-//    workgroup, enough to cover HBM latency at full bandwidth.
+//    stage, through a 3-deep ring: two stages (20 KiB) in flight per
+//    workgroup, ~10 MB over the chip.  Measured on the 58.7 MB decode
+//    shards, deeper rings (up to 6 stages, 30 MB in flight) were ~1 us
+//    slower per GEMV: the extra requests only queue at the memory.
 //  * Each wave owns 16 of the 64 columns.  The MFMA B operand (8 consecutive
 //    k of one column) comes from ds_read_b64_tr_b16 transpose reads of the
 //    [k][n] slab, the A operand (x) from ds_read_b128, and
@@ -35,7 +37,7 @@ namespace tpcol {
 
 static constexpr int GV_BN = 64;        // columns per workgroup strip
 static constexpr int GV_SLAB = 64;      // k rows per slab
-static constexpr int GV_STAGES = 7;     // ring depth
+static constexpr int GV_STAGES = 3;     // ring depth
 static constexpr int GV_NT = 256;       // 4 wave64
 static constexpr int GV_TARGET_WG = 512;
 static constexpr int GV_WSLAB = GV_SLAB * GV_BN;  // W elements per stage (8 KiB)

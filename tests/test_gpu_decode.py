@@ -81,3 +81,71 @@ def test_gemv_repeated_calls():
         tp.tp_row_linear_partial(Xd, Wd, P)
         torch().cuda.synchronize()
         assert np.array_equal(host(P), exact), it
+
+
+def _int_operands(M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.integers(-2, 3, size=(M, K)).astype(np.float32)
+    Wm = rng.integers(-2, 3, size=(K, N)).astype(np.float32)
+    Xd = dev(synth.Tensor(X, "bf16", synth.round_to_bf16_bits(X)))
+    Wd = dev(synth.Tensor(Wm, "bf16", synth.round_to_bf16_bits(Wm)))
+    return Xd, Wd, (X.astype(np.int64) @ Wm.astype(np.int64)).astype(np.float64)
+
+
+@pytest.mark.parametrize("fill", [0x00, 0xFF, "random"])
+def test_gemv_workspace_contents_do_not_matter(fill):
+    # the workspace is never cleared: whatever bytes it holds, every call
+    # writes the split-K partials it reads
+    note(f"gemv workspace fill {fill}")
+    T = torch()
+    Xd, Wd, exact = _int_operands(16, 4096, 1024, seed=7)
+    nbytes = tp.tp_row_linear_partial_workspace(tp.TP_BF16, 16, 4096, 1024)
+    assert nbytes > 0
+    ws = T.empty((nbytes,), dtype=T.uint8, device="cuda:0")
+    for it in range(3):
+        if fill == "random":
+            ws.copy_(T.randint(0, 256, (nbytes,), dtype=T.uint8, generator=T.Generator().manual_seed(it)))
+        else:
+            ws.fill_(fill)
+        P = empty((16, 1024), "f32", fill=float("nan"))
+        tp.tp_row_linear_partial(Xd, Wd, P, ws=ws)
+        torch().cuda.synchronize()
+        assert np.array_equal(host(P), exact), it
+
+
+def test_gemv_graph_replays_share_one_workspace():
+    # captured GEMVs replay against one workspace that the column and row
+    # GEMVs (different split counts) share, with eager calls in between
+    note("gemv graph replay")
+    T = torch()
+    Xd, W1, ex1 = _int_operands(16, 2048, 1536, seed=11)
+    _, W2, _ = _int_operands(16, 1536, 2048, seed=12)
+    nbytes = max(tp.tp_col_linear_gelu_workspace(tp.TP_BF16, tp.TP_ACT_NONE, 16, 2048, 1536),
+                 tp.tp_row_linear_partial_workspace(tp.TP_BF16, 16, 1536, 2048))
+    ws = T.empty((nbytes,), dtype=T.uint8, device="cuda:0")
+    H = empty((16, 1536), "bf16")
+    P = empty((16, 2048), "f32")
+
+    def step():
+        tp.tp_col_linear_gelu(Xd, W1, H, act="none", ws=ws)
+        tp.tp_row_linear_partial(H, W2, P, ws=ws)
+
+    step()
+    T.cuda.synchronize()
+    ref_P = host(P)
+    # H holds small integers (|h| <= 2 * 2048), exact in bf16 only where they fit
+    assert np.array_equal(host(H), synth.bf16_bits_to_f32(synth.round_to_bf16_bits(ex1)).astype(np.float64))
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        step()
+    T.cuda.synchronize()
+    for it in range(4):
+        H.fill_(float("nan"))
+        P.fill_(float("nan"))
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        assert np.array_equal(host(P), ref_P), it
+        step()
+        T.cuda.synchronize()
+        assert np.array_equal(host(P), ref_P), it
