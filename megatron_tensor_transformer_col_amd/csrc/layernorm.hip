@@ -40,15 +40,29 @@ rs_layernorm_kernel(LnPartials pp, int n, int64_t rows, int N, int64_t ldp, cons
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * LN_ROWS_PER_WG + (threadIdx.x >> 6);
   if (row >= rows) return;  // whole wave: no barrier in this kernel
-  // Loads of UNR shards are issued together before they are added (in shard
-  // order), so a wave keeps UNR * CH 16-byte loads in flight.
+  // Every load of the row is issued before the first store: Ysum or Y may
+  // share memory with the residual (an in-place update) or with gamma and
+  // beta as far as the compiler knows, so a load placed after a store would
+  // wait for it.  Loads of UNR shards are issued together before they are
+  // added (in shard order).  Short rows (CH <= 4) also fetch the residual,
+  // bias, gamma and beta with the first shard, so the row costs about one
+  // memory latency.
   constexpr int UNR = CH <= 4 ? 4 : (CH <= 16 ? 2 : 1);
-  f32x4_t x[CH];
+  constexpr bool EARLY = CH <= 4;
+  auto ld4 = [&](const float *base, int col) {
+    return col < N ? *reinterpret_cast<const f32x4_t *>(base + col) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  };
+  f32x4_t x[CH], r[EARLY ? CH : 1], bv[EARLY ? CH : 1], gm[EARLY ? CH : 1], bt[EARLY ? CH : 1];
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int col = (c * 64 + lane) * 4;
-    x[c] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    if (col < N) x[c] = *reinterpret_cast<const f32x4_t *>(pp.p[0] + row * ldp + col);
+    x[c] = ld4(pp.p[0] + row * ldp, col);
+    if constexpr (EARLY) {
+      r[c] = res != nullptr ? ld4(res + row * ldr, col) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      bv[c] = bias != nullptr ? ld4(bias, col) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      gm[c] = ld4(gamma, col);
+      bt[c] = ld4(beta, col);
+    }
   }
   for (int i0 = 1; i0 < n; i0 += UNR) {
     f32x4_t t[UNR][CH];
@@ -66,15 +80,32 @@ rs_layernorm_kernel(LnPartials pp, int n, int64_t rows, int N, int64_t ldp, cons
       for (int c = 0; c < CH; ++c)
         if (i0 + j < n) x[c] += t[j][c];
   }
+  // shard sum, then the bias, then the residual (the reference sum's order)
+  if constexpr (EARLY) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      if (bias != nullptr) x[c] += bv[c];
+      if (res != nullptr) x[c] += r[c];
+    }
+  } else {
+    if (bias != nullptr) {
+#pragma unroll
+      for (int c = 0; c < CH; ++c) x[c] += ld4(bias, (c * 64 + lane) * 4);
+    }
+    if (res != nullptr) {
+      f32x4_t rr[CH];  // all chunks loaded before the first Ysum store
+#pragma unroll
+      for (int c = 0; c < CH; ++c) rr[c] = ld4(res + row * ldr, (c * 64 + lane) * 4);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) x[c] += rr[c];
+    }
+  }
   float s = 0.f;
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int col = (c * 64 + lane) * 4;
     if (col < N) {
-      f32x4_t a = x[c];
-      if (bias != nullptr) a += *reinterpret_cast<const f32x4_t *>(bias + col);
-      if (res != nullptr) a += *reinterpret_cast<const f32x4_t *>(res + row * ldr + col);
-      x[c] = a;
+      const f32x4_t a = x[c];
       if (Ysum != nullptr) *reinterpret_cast<f32x4_t *>(Ysum + row * ldys + col) = a;
       s += (a[0] + a[1]) + (a[2] + a[3]);
     }
@@ -91,18 +122,32 @@ rs_layernorm_kernel(LnPartials pp, int n, int64_t rows, int N, int64_t ldp, cons
     }
   }
   const float rstd = 1.0f / sqrtf(wave_sum(q) * invN + eps);
+  // gamma / beta of GB chunks at a time, loaded before those chunks' stores
+  constexpr int GB = EARLY ? CH : 8;
 #pragma unroll
-  for (int c = 0; c < CH; ++c) {
-    const int col = (c * 64 + lane) * 4;
-    if (col < N) {
-      const f32x4_t g = *reinterpret_cast<const f32x4_t *>(gamma + col);
-      const f32x4_t b = *reinterpret_cast<const f32x4_t *>(beta + col);
-      const f32x4_t y = (x[c] - mean) * rstd * g + b;
-      if constexpr (OUT_BF16)
-        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + row * ldy + col) =
-            make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
-      else
-        *reinterpret_cast<f32x4_t *>(static_cast<float *>(Y) + row * ldy + col) = y;
+  for (int c0 = 0; c0 < CH; c0 += GB) {
+    f32x4_t g[GB], b[GB];
+#pragma unroll
+    for (int k = 0; k < GB; ++k) {
+      if constexpr (EARLY) {
+        g[k] = gm[c0 + k];
+        b[k] = bt[c0 + k];
+      } else {
+        g[k] = ld4(gamma, ((c0 + k) * 64 + lane) * 4);
+        b[k] = ld4(beta, ((c0 + k) * 64 + lane) * 4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < GB; ++k) {
+      const int col = ((c0 + k) * 64 + lane) * 4;
+      if (col < N) {
+        const f32x4_t y = (x[c0 + k] - mean) * rstd * g[k] + b[k];
+        if constexpr (OUT_BF16)
+          *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + row * ldy + col) =
+              make_uint2(pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3]));
+        else
+          *reinterpret_cast<f32x4_t *>(static_cast<float *>(Y) + row * ldy + col) = y;
+      }
     }
   }
 }
