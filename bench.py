@@ -255,6 +255,23 @@ class Rows:
         self.tp.tp_mlp_shard_backward(s["X"], s["Wg"], s["Wd"], s["dY"], s["dWg"], s["dWd"], s["dXi"],
                                       act="swiglu", Wup=s["Wu"], dWup=s["dWu"])
 
+    # ---- GPT-2-medium GELU MLP shard backward: T 8192, h 1024, ffn 4096 / 4
+    def gelu_mlp(self):
+        t = self.torch
+        T, h, f = 8192, 1024, 1024
+        s = {"X": self.randn((T, h), 1.0), "dY": self.randn((T, h), 1.0),
+             "W1": self.randn((h, f), 0.02), "W2": self.randn((f, h), 0.02), "b1": self.randn((f,), 0.02)}
+        s["dW1"] = self.empty((h, f), t.float32)
+        s["dW2"] = self.empty((f, h), t.float32)
+        s["db1"] = self.empty((f,), t.float32)
+        s["dXi"] = self.empty((T, h), t.float32)
+        s["flop_gemm"] = 2.0 * T * h * f
+        return s
+
+    def gelu_mlp_bwd(self, s):
+        self.tp.tp_mlp_shard_backward(s["X"], s["W1"], s["W2"], s["dY"], s["dW1"], s["dW2"], s["dXi"],
+                                      act="gelu", b1=s["b1"], db1=s["db1"])
+
     # ---- head-sharded MHA: b 4, s 2048, h 4096, 8 local heads of 128
     def mha(self):
         t = self.torch
@@ -407,6 +424,15 @@ def rows(torch, tp, steps, warmup):
                                "note": "algorithmic flops (dgrad x3 + wgrad x3); the Z recompute "
                                        "(+2 GEMMs) is not counted"}
     del s
+    s = R.gelu_mlp()
+    gg = graph_of(torch, lambda: R.gelu_mlp_bwd(s))
+    ms_g, _ = timed(torch, lambda kt: gg.replay(), s_ms, w_ms)
+    out["gpt2m_gelu_mlp_bwd"] = {"ms": ms_g, "tflops": 4 * s["flop_gemm"] / ms_g / 1e9,
+                                 "frac_peak": 4 * s["flop_gemm"] / ms_g / 1e9 / PEAK_BF16_TFLOPS,
+                                 "note": "one GPT-2-medium shard (T 8192, h 1024, ffn 1024 per shard): "
+                                         "algorithmic flops of dH, dW2, dW1, dX; the Z recompute and db1 "
+                                         "are not counted"}
+    del s
     s = R.mha()
     ga = graph_of(torch, lambda: R.attn(s))
     ms_a, _ = timed(torch, lambda kt: ga.replay(), s_ms, w_ms)
@@ -481,6 +507,9 @@ def run_op(torch, tp, synth, name, iters):
             s = R.swiglu()
             fn = {"c3_col": lambda: R.swiglu_col(s), "c3_down": lambda: R.swiglu_down(s),
                   "c3_bwd": lambda: R.swiglu_bwd(s)}[name]
+        elif name == "c11_mlp_bwd":
+            s = R.gelu_mlp()
+            fn = lambda: R.gelu_mlp_bwd(s)
         elif name == "c4_attn":
             s = R.mha()
             fn = lambda: R.attn(s)

@@ -111,8 +111,10 @@ bool use_gemv(int dtype, int64_t M) {
 // Backward workspace layout: dH [M x Ni], H [M x Ni], dZ [M x Ni] (GELU) or
 // [M x 2Ni] = [dZg | dZu] (SwiGLU); each region 256-byte aligned.
 struct BwdWs {
-  size_t dH, H, dZ, total;
+  size_t dH, H, dZ, cs, total;
 };
+// dH_i, H_i, dZ_i (SwiGLU: [dZg | dZu]); GELU / no activation also the
+// fp32 column-sum partials of db1
 BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
   const size_t e = esize(dtype);
   const size_t one = round256((size_t)M * (size_t)Ni * e);
@@ -120,7 +122,8 @@ BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
   w.dH = 0;
   w.H = one;
   w.dZ = 2 * one;
-  w.total = w.dZ + (act == TP_ACT_SWIGLU ? round256((size_t)M * 2 * (size_t)Ni * e) : one);
+  w.cs = w.dZ + (act == TP_ACT_SWIGLU ? round256((size_t)M * 2 * (size_t)Ni * e) : one);
+  w.total = w.cs + (act == TP_ACT_SWIGLU ? 0 : round256(colsum_workspace(Ni)));
   return w;
 }
 
@@ -664,6 +667,10 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
   void *dZ = base + L.dZ;
   const int64_t ldz = swiglu ? 2 * Ni : Ni;
   void *dZu = swiglu ? static_cast<void *>(base + L.dZ + (size_t)Ni * e) : nullptr;
+  // dH is dead once the recompute has formed dZ: its region then holds the
+  // split-K partials of the weight-gradient GEMMs
+  float *dHpart = M > 0 ? reinterpret_cast<float *>(base + L.dH) : nullptr;
+  const size_t dHpart_bytes = M > 0 ? L.H - L.dH : 0;
 
   if (M > 0) {
     // dH = dY W2^T  (row-parallel layer, input gradient of this shard's slice)
@@ -703,6 +710,7 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
     w.A = H; w.lda = Ni;
     w.B = dY; w.ldb = lddy;
     w.C = dW2; w.ldc = K;
+    w.part = dHpart; w.part_bytes = dHpart_bytes;
     TRY(hip_status(launch_gemm(w, s), "dW2 GEMM"));
   }
   // dW1 = X^T dZ (column-parallel weight gradient; dWup = X^T dZu)
@@ -713,6 +721,7 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
     w.A = X; w.lda = ldx;
     w.B = dZ; w.ldb = ldz;
     w.C = dW1; w.ldc = Ni;
+    w.part = dHpart; w.part_bytes = dHpart_bytes;
     TRY(hip_status(launch_gemm(w, s), "dW1 GEMM"));
     if (swiglu) {
       w.B = dZu;
@@ -720,7 +729,10 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
       TRY(hip_status(launch_gemm(w, s), "dWup GEMM"));
     }
   }
-  if (db1 != nullptr) TRY(hip_status(launch_colsum(dtype, M, Ni, dZ, ldz, db1, s), "db1"));
+  if (db1 != nullptr) {
+    float *cs = M > 0 ? reinterpret_cast<float *>(base + L.cs) : nullptr;  // M == 0: db1 = 0
+    TRY(hip_status(launch_colsum(dtype, M, Ni, dZ, ldz, db1, cs, s), "db1"));
+  }
 
   if (M > 0) {
     // dX_i = dZ W1^T  (SwiGLU: [dZg | dZu] [Wg | Wu]^T in one K-concatenated pass)

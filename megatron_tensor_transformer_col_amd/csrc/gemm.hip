@@ -272,6 +272,7 @@ static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
   p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K; p.K1 = (int)a.K1;
   p.tiles_m = (int)((a.M + BM - 1) / BM);
   p.tiles_n = (int)((a.N + BN - 1) / BN);
+  p.zstride = 0;
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n));
   hipLaunchKernelGGL((gemm_kernel<T, BM, BN, BK, WGM, WGN, LAYOUT, EPI, DUAL, KCAT>), grid,
                      dim3(WGM * WGN * 64), 0, s, p);
@@ -325,10 +326,45 @@ static hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+// K-range splits for a bf16 TN fp32 product with scratch: enough that the
+// 128 x 128 tiles times the splits fill about one round of 256 CUs, each
+// split at least 512 deep, the partials inside the scratch.
+static int split_k_factor(const GemmArgs &a) {
+  if (a.part == nullptr || a.layout != LAY_TN || a.epi != EPI_STORE_F32 || a.bias != nullptr || a.dual ||
+      a.kcat || a.dtype != DT_BF16)
+    return 1;
+  const int64_t tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (tiles >= 128) return 1;
+  const size_t one = (size_t)a.M * (size_t)a.N * sizeof(float);
+  int S = 1;
+  while (S < 8 && tiles * 2 * S <= 256 && (size_t)(2 * S) * one <= a.part_bytes && a.K % (64 * S) == 0 &&
+         a.K / (2 * S) >= 512)
+    S *= 2;
+  return S;
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.dtype == DT_BF16) {
-    const hipError_t e = launch_gemm_lds(a, s);
+    const int S = split_k_factor(a);
+    if (S > 1) {
+      GemmArgs b = a;
+      b.splits = S;
+      b.K = a.K / S;
+      b.C = a.part;
+      b.ldc = a.N;
+      b.zstride = a.M * a.N;
+      const hipError_t e = launch_gemm_lds(b, s);
+      if (e == hipSuccess) {
+        const float *parts[8];
+        for (int z = 0; z < S; ++z) parts[z] = a.part + (int64_t)z * b.zstride;
+        return launch_shard_sum(DT_F32, a.M, a.N, S, parts, a.N, nullptr, a.C, a.ldc, s);
+      }
+      if (e != hipErrorNotSupported) return e;
+    }
+    GemmArgs b = a;
+    b.splits = 1;
+    const hipError_t e = launch_gemm_lds(b, s);
     if (e != hipErrorNotSupported) return e;
     return dispatch<uint16_t>(a, s);
   }

@@ -17,8 +17,9 @@ struct GemmParams {
   void *C; int64_t ldc;
   void *C2; int64_t ldc2;
   void *C3; int64_t ldc3;
-  int M, N, K, K1;
+  int M, N, K, K1;  // K: depth of one K-range split
   int tiles_m, tiles_n;
+  int64_t zstride;   // elements between split outputs (TN split-K only)
 };
 
 template <typename T>

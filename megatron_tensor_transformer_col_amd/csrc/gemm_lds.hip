@@ -144,7 +144,8 @@ __device__ __forceinline__ uint4 frag_mn(const uint16_t *t, int kc, int c0, int 
 // wave on each SIMD covers the LDS latency.
 template <int BM, int BN, int LBK, int WGM, int WGN, int LAYOUT, int EPI, bool DUAL, bool KCAT,
           int STAGES, bool PREFETCH>
-__global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) {
+__global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams pin) {
+  GemmParams p = pin;
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -169,9 +170,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
   constexpr int SROW = BN * OES + 16;               // staged row bytes (16-byte pad)
   constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32 || EPI == EPI_SWIGLU) &&
                           BM * SROW <= 144 * 1024;
-  // The SwiGLU backward (three bf16 outputs, dH read) stages its outputs one
-  // tile at a time the same way.
-  constexpr bool STAGED3 = EPI == EPI_SWIGLU_BWD && 2 * BM * (BN * 2 + 16) <= 144 * 1024;
+  // The activation backward epilogues (dH read; GELU: dZ and H written,
+  // SwiGLU: dZg, dZu and H) stage dH and then their outputs one tile at a
+  // time the same way.  Reading dH element by element between the stores
+  // would serialise: every load waits for the stores before it, which the
+  // compiler cannot prove do not overlap it.
+  constexpr bool STAGED3 = (EPI == EPI_SWIGLU_BWD || EPI == EPI_GELU_BWD) && 2 * BM * (BN * 2 + 16) <= 144 * 1024;
+  constexpr int NOUT = EPI == EPI_SWIGLU_BWD ? 3 : 2;
   constexpr int RING_EL = STAGES * STAGE;
   constexpr int STG_EL = STAGED ? BM * SROW / 2 : (STAGED3 ? BM * (BN * 2 + 16) : 0);
   __shared__ __attribute__((aligned(1024))) uint16_t smem[RING_EL > STG_EL ? RING_EL : STG_EL];
@@ -188,6 +193,14 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
 
   const uint16_t *Ag = static_cast<const uint16_t *>(p.A);
   const uint16_t *Bg = static_cast<const uint16_t *>(p.B);
+  if constexpr (LAYOUT == LAY_TN) {
+    // split-K: grid row z takes K rows [z K, (z+1) K) of both operands and
+    // writes its own fp32 partial
+    const int z = blockIdx.y;
+    Ag += (int64_t)z * p.K * p.lda;
+    Bg += (int64_t)z * p.K * p.ldb;
+    p.C = static_cast<float *>(p.C) + (int64_t)z * p.zstride;
+  }
   const uint16_t *B2g = static_cast<const uint16_t *>(p.B2);
 
   ATile ta;
@@ -373,13 +386,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
   }
   if constexpr (STAGED3) {
     // dH comes into LDS by coalesced 16-byte loads; then each output tile
-    // (dZg, dZu, H) in turn is computed from the accumulators and dH, written
-    // to LDS and stored as whole row chunks.
+    // (GELU: dZ, H; SwiGLU: dZg, dZu, H) in turn is computed from the
+    // accumulators and dH, written to LDS and stored as whole row chunks.
     constexpr int SR = BN * 2 + 16;  // staged row bytes
     constexpr int CPR = BN * 2 / 16;
     char *dhs = reinterpret_cast<char *>(smem);
     char *out = dhs + BM * SR;
-    if (p.bias != nullptr) {  // the bias belongs to the gate pre-activation
+    if (p.bias != nullptr) {  // the bias belongs to the (gate) pre-activation
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         const int col = n0 + wn * WTN + j * 16 + g * 4;
@@ -402,7 +415,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
     }
     __syncthreads();
 #pragma unroll
-    for (int which = 0; which < 3; ++which) {  // 0: dZg, 1: dZu, 2: H
+    for (int which = 0; which < NOUT; ++which) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
@@ -412,17 +425,23 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams p) 
           load4(reinterpret_cast<const uint16_t *>(dhs + off), dh);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float gt = acc[i][j][r], ut = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
-            const float sg = sigmoid_f(gt);
-            const float sl = gt * sg;
-            o[r] = which == 0 ? dh[r] * ut * (sg * (1.0f + gt * (1.0f - sg))) : (which == 1 ? dh[r] * sl : sl * ut);
+            const float gt = acc[i][j][r];
+            if constexpr (EPI == EPI_GELU_BWD) {
+              o[r] = which == 0 ? dh[r] * gelu_grad_f(gt) : gelu_f(gt);
+            } else {
+              const float ut = acc2[DUAL ? i : 0][DUAL ? j : 0][r];
+              const float sg = sigmoid_f(gt);
+              const float sl = gt * sg;
+              o[r] = which == 0 ? dh[r] * ut * (sg * (1.0f + gt * (1.0f - sg))) : (which == 1 ? dh[r] * sl : sl * ut);
+            }
           }
           store4(reinterpret_cast<uint16_t *>(out + off), o);
         }
       }
       __syncthreads();
-      void *C = which == 0 ? p.C : (which == 1 ? p.C3 : p.C2);
-      const int64_t ldc = which == 0 ? p.ldc : (which == 1 ? p.ldc3 : p.ldc2);
+      // SwiGLU: dZg -> C, dZu -> C3, H -> C2; GELU: dZ -> C, H -> C2
+      void *C = which == 0 ? p.C : (which == NOUT - 1 ? p.C2 : p.C3);
+      const int64_t ldc = which == 0 ? p.ldc : (which == NOUT - 1 ? p.ldc2 : p.ldc3);
       for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
         const int rl = c / CPR, cc = c % CPR;
         const int row = m0 + rl, col = n0 + cc * 8;
@@ -468,9 +487,10 @@ static hipError_t run_lds(const GemmArgs &a, hipStream_t s) {
   p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K; p.K1 = (int)a.K1;
   p.tiles_m = (int)((a.M + BM - 1) / BM);
   p.tiles_n = (int)((a.N + BN - 1) / BN);
+  p.zstride = a.zstride;
   hipLaunchKernelGGL(
       (gemm_lds_kernel<BM, BN, LBK, WGM, WGN, LAYOUT, EPI, DUAL, KCAT, STAGES, PREFETCH>),
-      dim3((unsigned)(p.tiles_m * p.tiles_n)), dim3(WGM * WGN * 64), 0, s, p);
+      dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)a.splits), dim3(WGM * WGN * 64), 0, s, p);
   return hipGetLastError();
 }
 
@@ -518,7 +538,8 @@ hipError_t launch_gemm_lds(const GemmArgs &a, hipStream_t s) {
   if (a.dtype != DT_BF16 || a.K <= 0 || a.K % LBK != 0) return hipErrorNotSupported;
   if (a.kcat && a.K1 % LBK != 0) return hipErrorNotSupported;
   // small problems stay on the general kernel (more, smaller tiles)
-  if (((a.M + 127) / 128) * ((a.N + 127) / 128) < 64) return hipErrorNotSupported;
+  if (((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits < 64) return hipErrorNotSupported;
+  if (a.splits > 1 && (a.layout != LAY_TN || a.epi != EPI_STORE_F32)) return hipErrorInvalidValue;
   if (a.M < 8 || a.N < 8) return hipErrorNotSupported;
   switch (a.layout) {
     case LAY_NN:

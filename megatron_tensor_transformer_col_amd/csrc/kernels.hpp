@@ -39,6 +39,14 @@ struct GemmArgs {
   void *C = nullptr;  int64_t ldc = 0;
   void *C2 = nullptr; int64_t ldc2 = 0;
   void *C3 = nullptr; int64_t ldc3 = 0;
+  // Optional fp32 scratch for split-K of TN fp32 products whose output has
+  // too few tiles to fill the chip (weight gradients of narrow shards):
+  // launch_gemm then writes `splits` K-range partials [splits][M][N] there
+  // and adds them into C in split order.
+  float *part = nullptr; size_t part_bytes = 0;
+  // set by launch_gemm for the LDS kernel: K-range splits (grid y) and the
+  // element stride between their outputs
+  int splits = 1; int64_t zstride = 0;
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
@@ -92,7 +100,8 @@ hipError_t launch_vocab_loss(int dtype, int64_t T, int64_t Vi, int64_t v0, const
                              const int32_t *targets, const float *lse, float *row_loss, float *shard_loss,
                              hipStream_t s);
 hipError_t launch_vocab_total(int n, const float *const *losses, float *total, hipStream_t s);
+size_t colsum_workspace(int64_t N);  // fp32 partial bytes launch_colsum needs
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,
-                         hipStream_t s);
+                         float *part, hipStream_t s);
 
 }  // namespace tpcol

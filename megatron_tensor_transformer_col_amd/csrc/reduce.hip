@@ -61,36 +61,111 @@ hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const fl
   return hipGetLastError();
 }
 
-// db[c] = sum_m dZ[m][c].  Workgroup = 64 columns x 4 row-slices; the four
-// slice sums are combined in LDS in a fixed order.
+// db[c] = sum_m dZ[m][c] in two passes, each in a fixed order.
+// Pass 1: workgroup (y, column block) = 256 threads = 32 16-byte column
+// vectors x 8 row lanes over the rows of split y; a thread adds rows
+// lane, lane + 8, ... of its vector in row order (4 loads in flight), the 8
+// lanes are added in lane order through LDS, and the sums go to part[y][c].
+// Pass 2: db[c] = sum over y of part[y][c] in split order.
+static constexpr int CS_MAX_SPLITS = 64;
+static constexpr int CS_MIN_ROWS = 64;  // rows per split at least
+
+static int colsum_splits(int64_t M) {
+  const int64_t s = (M + CS_MIN_ROWS - 1) / CS_MIN_ROWS;
+  return (int)(s < 1 ? 1 : (s > CS_MAX_SPLITS ? CS_MAX_SPLITS : s));
+}
+
+size_t colsum_workspace(int64_t N) { return (size_t)CS_MAX_SPLITS * (size_t)(N > 0 ? N : 0) * sizeof(float); }
+
 template <typename T>
 __global__ void __launch_bounds__(256)
-colsum_kernel(int64_t M, int64_t N, const T *dZ, int64_t ldz, float *db) {
-  __shared__ float part[4][64];
-  const int c = blockIdx.x * 64 + (threadIdx.x & 63);
-  const int slice = threadIdx.x >> 6;
-  float acc = 0.f;
-  if (c < N) {
-    for (int64_t m = slice; m < M; m += 4) acc += Elem<T>::to_f(dZ[m * ldz + c]);
+colsum_partial_kernel(int64_t M, int64_t N, const T *__restrict__ dZ, int64_t ldz, int64_t rows_per,
+                      float *__restrict__ part) {
+  constexpr int VW = Elem<T>::VW;
+  __shared__ float red[8][32 * VW];
+  const int vc = threadIdx.x & 31, lr = threadIdx.x >> 5;
+  const int64_t c0 = ((int64_t)blockIdx.x * 32 + vc) * VW;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+  const int64_t r1 = M < r0 + rows_per ? M : r0 + rows_per;
+  float acc[VW];
+#pragma unroll
+  for (int k = 0; k < VW; ++k) acc[k] = 0.f;
+  auto add = [&](const uint4 &u) {
+    if constexpr (VW == 8) {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += bf2f((uint16_t)(w[k] & 0xffffu));
+        acc[2 * k + 1] += bf2f((uint16_t)(w[k] >> 16));
+      }
+    } else {
+      acc[0] += __uint_as_float(u.x); acc[1] += __uint_as_float(u.y);
+      acc[2] += __uint_as_float(u.z); acc[3] += __uint_as_float(u.w);
+    }
+  };
+  if (c0 < N) {
+    const T *col = dZ + c0;
+    int64_t m = r0 + lr;
+    for (; m + 24 < r1; m += 32) {
+      uint4 v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const uint4 *>(col + (m + 8 * q) * ldz);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) add(v[q]);
+    }
+    for (; m < r1; m += 8) add(*reinterpret_cast<const uint4 *>(col + m * ldz));
   }
-  part[slice][threadIdx.x & 63] = acc;
+#pragma unroll
+  for (int k = 0; k < VW; ++k) red[lr][vc * VW + k] = acc[k];
   __syncthreads();
-  if (slice == 0 && c < N) {
-    const int t = threadIdx.x & 63;
-    db[c] = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+  if (lr == 0 && c0 < N) {
+#pragma unroll
+    for (int k = 0; k < VW; ++k) {
+      float t = red[0][vc * VW + k];
+#pragma unroll
+      for (int l = 1; l < 8; ++l) t += red[l][vc * VW + k];
+      part[(int64_t)blockIdx.y * N + c0 + k] = t;
+    }
   }
 }
 
+__global__ void __launch_bounds__(256)
+colsum_final_kernel(int splits, int64_t N, const float *__restrict__ part, float *__restrict__ db) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= N) return;
+  float t = 0.f;
+  for (int y0 = 0; y0 < splits; y0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = y0 + j < splits ? part[(int64_t)(y0 + j) * N + c] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (y0 + j < splits) t += v[j];
+  }
+  db[c] = t;
+}
+
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,
-                         hipStream_t s) {
+                         float *part, hipStream_t s) {
   if (N <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((N + 63) / 64));
-  if (dtype == DT_BF16)
-    hipLaunchKernelGGL(colsum_kernel<uint16_t>, grid, dim3(256), 0, s, M, N,
-                       static_cast<const uint16_t *>(dZ), ldz, db);
-  else
-    hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, M, N,
-                       static_cast<const float *>(dZ), ldz, db);
+  int splits = 0;
+  if (M > 0) {
+    splits = colsum_splits(M);
+    const int64_t rows_per = (M + splits - 1) / splits;
+    splits = (int)((M + rows_per - 1) / rows_per);
+    const int vw = dtype == DT_BF16 ? 8 : 4;
+    const dim3 grid((unsigned)((N + 32 * vw - 1) / (32 * vw)), (unsigned)splits);
+    if (dtype == DT_BF16)
+      hipLaunchKernelGGL(colsum_partial_kernel<uint16_t>, grid, dim3(256), 0, s, M, N,
+                         static_cast<const uint16_t *>(dZ), ldz, rows_per, part);
+    else
+      hipLaunchKernelGGL(colsum_partial_kernel<float>, grid, dim3(256), 0, s, M, N,
+                         static_cast<const float *>(dZ), ldz, rows_per, part);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, splits, N,
+                     part, db);
   return hipGetLastError();
 }
 

@@ -128,7 +128,12 @@ def test_mlp_gelu_bf16_medium(T_, h, ffn, n):
 
 @pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (1030, 512, 1024, 1),
                                         # token count % 64 == 0: every GEMM on the LDS-DMA kernel
-                                        (1024, 1024, 2048, 2)])
+                                        (1024, 1024, 2048, 2),
+                                        # db1: 64 row splits of 65 rows, ragged last split
+                                        (4160, 256, 512, 1),
+                                        # weight gradients [512 x 1024]: 32 tiles, 4 K-range
+                                        # splits added in order from the dead dH scratch
+                                        (4096, 512, 1024, 1)])
 def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     note(f"bf16 MLP GELU bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_mlp_inputs(T_, h, ffn, "bf16", seed=2, with_dy=True, with_bias=True)
