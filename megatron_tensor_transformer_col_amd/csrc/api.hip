@@ -285,6 +285,9 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
     g.A = O; g.lda = w;
     g.B = dY; g.ldb = lddy;
     g.C = dWo; g.ldc = h;
+    // dQKV_i and the head-split partials are written only by the attention
+    // kernels below: until then their regions hold split-K partials
+    g.part = reinterpret_cast<float *>(dqkv); g.part_bytes = L.total - L.dqkv;
     TRY(hip_status(launch_gemm(g, st), "dWo GEMM"));
   }
   if (T > 0)

@@ -327,14 +327,19 @@ static hipError_t dispatch(const GemmArgs &a, hipStream_t s) {
 }
 
 // K-range splits for a bf16 TN fp32 product with scratch: enough that the
-// 128 x 128 tiles times the splits fill about one round of 256 CUs, each
-// split at least 512 deep, the partials inside the scratch.
+// workgroups of the tile configuration the LDS kernel picks (256 x 256 from
+// 192 tiles up, else 128 x 256 from 128 tiles up, else 128 x 128) times the
+// splits fill about one round of 256 CUs, each split at least 512 deep, the
+// partials inside the scratch.
 static int split_k_factor(const GemmArgs &a) {
   if (a.part == nullptr || a.layout != LAY_TN || a.epi != EPI_STORE_F32 || a.bias != nullptr || a.dual ||
       a.kcat || a.dtype != DT_BF16)
     return 1;
-  const int64_t tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-  if (tiles >= 128) return 1;
+  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256);
+  const int64_t t128x256 = ((a.M + 127) / 128) * ((a.N + 255) / 256);
+  if (t256 >= 192) return 1;
+  const int64_t tiles = t128x256 >= 128 ? t128x256 : ((a.M + 127) / 128) * ((a.N + 127) / 128);
+  if (tiles > 128) return 1;
   const size_t one = (size_t)a.M * (size_t)a.N * sizeof(float);
   int S = 1;
   while (S < 8 && tiles * 2 * S <= 256 && (size_t)(2 * S) * one <= a.part_bytes && a.K % (64 * S) == 0 &&
