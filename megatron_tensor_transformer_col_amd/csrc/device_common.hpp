@@ -84,8 +84,20 @@ __device__ __forceinline__ PhiResult normal_cdf_pdf(float z) {
   return r;
 }
 
-// Exact-form GELU z * Phi(z) ("张量并行", MLP 层的并行化).
-__device__ __forceinline__ float gelu_f(float z) { return z * normal_cdf_pdf(z).phi_cdf; }
+// Exact-form GELU z * Phi(z) ("张量并行", MLP 层的并行化): the same 7.1.26
+// evaluation with its constants folded (1/sqrt 2 into p and into the
+// exponent, the 1/2 of Phi into the polynomial), two VALU operations fewer
+// per element than going through normal_cdf_pdf.
+__device__ __forceinline__ float gelu_f(float z) {
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, fabsf(z), 1.0f));
+  float hp = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  hp = fmaf(t, hp, 0.5f * 1.421413741f);
+  hp = fmaf(t, hp, 0.5f * -0.284496736f);
+  hp = fmaf(t, hp, 0.5f * 0.254829592f);
+  hp *= t;
+  const float hq = hp * __builtin_amdgcn_exp2f(z * z * (-0.5f * 1.4426950408889634f));  // erfc(|z|/sqrt 2) / 2
+  return z * (z >= 0.0f ? 1.0f - hq : hq);
+}
 // d/dz GELU = Phi(z) + z phi(z)
 __device__ __forceinline__ float gelu_grad_f(float z) {
   const PhiResult r = normal_cdf_pdf(z);
