@@ -133,7 +133,9 @@ def test_mlp_gelu_bf16_medium(T_, h, ffn, n):
                                         (4160, 256, 512, 1),
                                         # weight gradients [512 x 1024]: 32 tiles, 4 K-range
                                         # splits added in order from the dead dH scratch
-                                        (4096, 512, 1024, 1)])
+                                        (4096, 512, 1024, 1),
+                                        # ragged [264 x 520] weight gradients, 8 splits
+                                        (8192, 264, 520, 1)])
 def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     note(f"bf16 MLP GELU bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_mlp_inputs(T_, h, ffn, "bf16", seed=2, with_dy=True, with_bias=True)
