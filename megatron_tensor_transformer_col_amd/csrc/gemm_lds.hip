@@ -186,6 +186,7 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams pin
   const int wm = wave % WGM, wn = wave / WGM;
   const int M = p.M, N = p.N;
   const int nk = p.K / LBK;
+  constexpr bool PRIO = BM == 256 && LAYOUT != LAY_TN && !KCAT;
 
   int tm, tn;
   tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
@@ -338,7 +339,13 @@ __global__ void __launch_bounds__(WGM * WGN * 64) gemm_lds_kernel(GemmParams pin
       __syncthreads();
       if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
       load_frags(F, kt % STAGES);
+      // 256 x 256 NN / NT tiles: a wave issuing its MFMAs takes issue
+      // priority over the other wave of its SIMD (still reading fragments or
+      // issuing DMA), which keeps the matrix pipe fed: 1-4% on the Llama and
+      // MHA shapes; TN and K-concatenated tiles measured no gain.
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(1);
       mma(F);
+      if constexpr (PRIO) __builtin_amdgcn_s_setprio(0);
     }
   }
 
