@@ -505,10 +505,14 @@ static hipError_t run_lds(const GemmArgs &a, hipStream_t s) {
 // workgroup (two per SIMD, so LDS and DMA latency of one wave hides under
 // the other's MFMAs) and 256-wide tiles to cut L2 -> CU traffic per flop.
 static int64_t cu_count() {
+  // the attribute query is cached per host thread for its current device
+  thread_local int cached_dev = -1, cached_n = 0;
   int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-    return 256;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev == cached_dev) return cached_n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  cached_dev = dev;
+  cached_n = n;
   return n;
 }
 
@@ -520,6 +524,16 @@ static hipError_t pick_lds(const GemmArgs &a, hipStream_t s) {
     // four 40 KiB stages fill the 160 KiB of LDS (one workgroup per CU
     // either way: its 8 waves take all the VGPRs); measured 2-8% faster than
     // two or three stages on the Llama SwiGLU shard
+    if constexpr (EPI == EPI_STORE_F32 && LAYOUT == LAY_NN) {
+      // mid-size fp32 NN products (the row-parallel partial of a narrow
+      // shard): 128 x 128 tiles stage in 67 KiB, so two workgroups share a
+      // CU and one's fp32 stores overlap the other's loop (8192 x 1024 x
+      // 1024: 23.9 -> 23.1 us; NT and split TN products measured slower)
+      const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+      const int64_t cus = cu_count();
+      if (a.splits == 1 && t128 >= cus && t128 <= 2 * cus)
+        return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
+    }
     if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
     return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
   } else {
@@ -534,6 +548,16 @@ static hipError_t pick_lds(const GemmArgs &a, hipStream_t s) {
       const double c128 = (double)((t128x256 + cus - 1) / cus) * (32768.0 / 1122.0);
       if (c256 <= c128) return run_lds<256, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
       return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
+    }
+    if constexpr (EPI == EPI_STORE_F32 && LAYOUT == LAY_NN) {
+      // mid-size fp32 NN products (the row-parallel partial of a narrow
+      // shard): 128 x 128 tiles stage in 67 KiB, so two workgroups share a
+      // CU and one's fp32 stores overlap the other's loop (8192 x 1024 x
+      // 1024: 23.9 -> 23.1 us; NT and split TN products measured slower)
+      const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128);
+      const int64_t cus = cu_count();
+      if (a.splits == 1 && t128 >= cus && t128 <= 2 * cus)
+        return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
     }
     if (t128x256 >= 128) return run_lds<128, 256, 32, 2, 4, LAYOUT, EPI, DUAL, KCAT, 4, false>(a, s);
     return run_lds<128, 128, 32, 2, 2, LAYOUT, EPI, DUAL, KCAT, 3, false>(a, s);
