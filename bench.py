@@ -610,8 +610,8 @@ def cpu_baseline(synth, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "exchange is not part of this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library computes one "
+              "GPU's shard and has no cross-GPU exchange", file=sys.stderr)
         sys.exit(2)
     import torch
     import megatron_tensor_transformer_col_amd as tp
