@@ -240,3 +240,27 @@ def test_llama_swiglu_full_size_sampled():
     assert_close(host(dWg[:, ci]), gw["dWg"], "bf16", "dWg_0 cols")
     assert_close(host(dWu[:, ci]), gw["dWu"], "bf16", "dWu_0 cols")
     assert_close(host(dWd[ci]), gw["dWd"], "bf16", "dWd_0 rows")
+
+
+def test_mlp_backward_repeats_bitwise():
+    # split-K weight gradients (4 splits here) and db1 add their partials in a
+    # fixed order: repeated calls give identical bits, whatever the
+    # workspace held before
+    note("bf16 MLP GELU bwd repeatability 4096x512x1024")
+    T = torch()
+    d = synth.make_mlp_inputs(4096, 512, 1024, "bf16", seed=5, with_dy=True, with_bias=True)
+    X, W1, W2, dY, b1 = dev(d["X"]), dev(d["W1"]), dev(d["W2"]), dev(d["dY"]), dev(d["b1"])[0]
+    nbytes = tp.tp_mlp_shard_backward_workspace(tp.TP_BF16, tp.TP_ACT_GELU_ERF, 4096, 1024)
+    ws = T.empty((nbytes,), dtype=T.uint8, device="cuda:0")
+    runs = []
+    for it in range(3):
+        ws.fill_(it * 85)
+        o = {"dW1": empty((512, 1024), "f32"), "dW2": empty((1024, 512), "f32"),
+             "dX": empty((4096, 512), "f32"), "db1": empty((1, 1024), "f32")}
+        tp.tp_mlp_shard_backward(X, W1, W2, dY, o["dW1"], o["dW2"], o["dX"], act="gelu", b1=b1,
+                                 db1=o["db1"][0], ws=ws)
+        T.cuda.synchronize()
+        runs.append({k: v.clone() for k, v in o.items()})
+    for r in runs[1:]:
+        for k in r:
+            assert T.equal(r[k], runs[0][k]), k
