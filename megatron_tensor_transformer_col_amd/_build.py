@@ -30,6 +30,10 @@ HIPCC_FLAGS = [
 # ordinary VGPRs (its softmax reads and rescales them every key block)
 EXTRA_FLAGS = {
     "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # the minimal-register scheduling strategy keeps the 64-deep GEMM's
+    # accumulators in place (the default one copied them between AGPRs and
+    # VGPRs inside the main loop)
+    "gemm_k64.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-minreg"],
 }
 
 

@@ -348,6 +348,14 @@ static int split_k_factor(const GemmArgs &a) {
   return S;
 }
 
+// bf16 products on the LDS-DMA kernels: 64-deep slabs where they apply,
+// else 32-deep ones
+static hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
+  const hipError_t e = launch_gemm_k64(a, s);
+  if (e != hipErrorNotSupported) return e;
+  return launch_gemm_lds(a, s);
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.dtype == DT_BF16) {
@@ -359,7 +367,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
       b.C = a.part;
       b.ldc = a.N;
       b.zstride = a.M * a.N;
-      const hipError_t e = launch_gemm_lds(b, s);
+      const hipError_t e = launch_lds(b, s);
       if (e == hipSuccess) {
         const float *parts[8];
         for (int z = 0; z < S; ++z) parts[z] = a.part + (int64_t)z * b.zstride;
@@ -369,7 +377,7 @@ hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
     }
     GemmArgs b = a;
     b.splits = 1;
-    const hipError_t e = launch_gemm_lds(b, s);
+    const hipError_t e = launch_lds(b, s);
     if (e != hipErrorNotSupported) return e;
     return dispatch<uint16_t>(a, s);
   }

@@ -1,0 +1,494 @@
+// bf16 MFMA GEMM for gfx950 with 64-deep K slabs, four waves per workgroup.
+//
+//   C[M x N] = A[M x K] . B[K x N]   (fp32 accumulate, K a multiple of 64)
+//
+// Same operand layouts (NN, NT, TN) and fused epilogues as the other GEMM
+// kernels; the design choices, each measured on MI355X:
+//
+//  * 64-deep slabs.  A k-contiguous operand row then contributes 128 bytes
+//    per slab, a whole cache line, so every L2 request of the HBM -> LDS DMA
+//    carries a full line; with 32-deep slabs half of them were 64-byte
+//    half-lines and the DMA topped out near 18 TB/s instead of ~23.
+//  * Four wave64 per workgroup (one per SIMD) with large per-wave tiles
+//    (64 x 64 or 128 x 128), accumulators in AGPRs.  The next 32-deep chunk's
+//    fragments are read from LDS while the current chunk's MFMAs run
+//    (two register sets), and one barrier per slab sits between a slab's two
+//    chunks, where every wave has finished reading the slab before.
+//  * 128 x 128 tiles run two workgroups per CU: while one is in its
+//    epilogue (activation, staging, stores) the other keeps the matrix cores
+//    busy, which hides the erf-GELU of the column-parallel product.  256 x 256
+//    tiles (one workgroup per CU) serve products with whole rounds of them.
+//  * The compiler's register allocation is steered with the minimal-register
+//    scheduling strategy (build flag); the default one shuffled accumulators
+//    between AGPRs and VGPRs inside the loop.
+//
+// Operand staging in LDS (each stage one 64-deep slab of A and of B):
+//  * k-contiguous rows (A in NN/NT, B in NT): 128 bytes = 8 granules of 16 B,
+//    granule c of row r stored at slot c ^ swz_k(r); fragments by
+//    ds_read_b128 (8 consecutive k of one row per lane).
+//  * m/n-contiguous rows (B in NN, A and B in TN): 64 k-rows as in HBM with
+//    the granule index XOR-swizzled by the row; the MFMA operand (8
+//    consecutive k of one column) comes from two ds_read_b64_tr_b16.
+//  * Rows / columns past M / N are clamped to the last valid one on load
+//    (their results are never stored), so no load leaves the operands.
+#include <algorithm>
+#include <type_traits>
+
+#include "gemm_common.hpp"
+#include "lds_dma.hpp"
+
+namespace tpcol {
+namespace k64 {
+
+constexpr int LBK = 64;  // slab depth
+constexpr int NW = 4;    // waves per workgroup
+
+// device-scope (write-through) 16-byte store from LDS; see gemm_lds.hip
+typedef unsigned int u32x4_wt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_wt(void *dst, const void *lds_src) {
+  const u32x4_wt v = *reinterpret_cast<const u32x4_wt *>(lds_src);
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(dst), "v"(v) : "memory");
+}
+
+// k-contiguous 128-byte rows: slot of granule c in row r is c ^ swz_k(r)
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+// m/n-contiguous rows: granule index bits 1..3 XOR-ed with row bits
+__device__ __forceinline__ int swz_mn(int r) { return ((r & 3) | (((r >> 3) & 1) << 2)) << 1; }
+
+// DMA of a k-contiguous operand slab: ROWS rows x 64 k (8 rows per KiB).
+// Per-lane 32-bit offsets relative to the tile's first row; the slab's
+// base pointer is wave-uniform (SGPRs).  KCAT: rows of the second source
+// (k >= K1) have their own offsets.
+template <int ROWS, bool KCAT>
+struct KDma {
+  static constexpr int PER_WAVE = ROWS / 8 / NW;
+  static_assert(ROWS % (8 * NW) == 0, "rows");
+  uint32_t off[PER_WAVE];
+  uint32_t off2[KCAT ? PER_WAVE : 1];
+  __device__ __forceinline__ void init(int64_t ld, int64_t ld2, int row0, int rows_lim, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int row = (wave + NW * j) * 8 + lane / 8;
+      const int c = (lane % 8) ^ swz_k(row);
+      const int64_t gr = min(row0 + row, rows_lim - 1) - row0;
+      off[j] = (uint32_t)(gr * ld * 2 + c * 16);
+      if constexpr (KCAT) off2[j] = (uint32_t)(gr * ld2 * 2 + c * 16);
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t *base, bool second, uint32_t lds, int wave) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const uint32_t o = (KCAT && second) ? off2[KCAT ? j : 0] : off[j];
+      dma16s(o, base, lds + (wave + NW * j) * 1024);
+    }
+  }
+};
+
+// DMA of an m/n-contiguous operand slab: 64 k-rows x COLS.
+template <int COLS>
+struct NDma {
+  static constexpr int GPR = COLS / 8;    // granules per row
+  static constexpr int RPB = 64 / GPR;    // rows per KiB
+  static constexpr int PER_WAVE = LBK / RPB / NW;
+  static_assert(GPR >= 16 && (LBK / RPB) % NW == 0, "cols");
+  uint32_t off[PER_WAVE];
+  __device__ __forceinline__ void init(int64_t ld, int col0, int col_lim, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int row = (wave + NW * j) * RPB + lane / GPR;
+      const int lg = (lane % GPR) ^ swz_mn(row);
+      const int col = min(col0 + lg * 8, col_lim - 8) - col0;
+      off[j] = (uint32_t)((int64_t)row * ld * 2 + col * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const uint16_t *base, uint32_t lds, int wave) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) dma16s(off[j], base, lds + (wave + NW * j) * 1024);
+  }
+};
+
+// Per-lane LDS byte offsets of one operand's fragments inside a stage, for
+// chunk kc (0/1) and fragment f (16 rows / columns each).
+template <bool KTYPE, int SPAN, int WT>
+struct FragAddr {
+  static constexpr int NF = WT / 16;
+  uint32_t off[2][KTYPE ? 1 : NF];
+  __device__ __forceinline__ void init(uint32_t region, int first, int lane) {
+    const int g = lane >> 4, l16 = lane & 15;
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      if constexpr (KTYPE) {
+        const int row = first + l16;  // + 16 f: swz_k only reads row bits 1..3
+        off[kc][0] = region + (uint32_t)(row * 128 + (((kc * 4 + g) ^ swz_k(row)) << 4));
+      } else {
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int r1 = kc * 32 + 8 * g + (l16 >> 2);
+          const int col = first + f * 16 + 4 * (l16 & 3);
+          const int o = (((col >> 3) ^ swz_mn(r1)) << 3) + (col & 4);  // swz_mn(r1) == swz_mn(r1 + 4)
+          off[kc][f] = region + (uint32_t)((r1 * SPAN + o) * 2);
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ uint4 read(const char *stage, int kc, int f) const {
+    if constexpr (KTYPE) {
+      return *reinterpret_cast<const uint4 *>(stage + off[kc][0] + f * 2048);
+    } else {
+      const uint16_t *q = reinterpret_cast<const uint16_t *>(stage + off[kc][f]);
+      const uint2 x = tr_read(q);
+      const uint2 y = tr_read(q + 4 * SPAN);
+      return make_uint4(x.x, x.y, y.x, y.y);
+    }
+  }
+};
+
+// BM x BN tile per workgroup of 4 waves (WGM x WGN), STAGES-deep ring of
+// 64-deep slabs, OCC workgroups per CU.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+gemm_k64_kernel(GemmParams pin) {
+  GemmParams p = pin;
+  static_assert(WGM * WGN == NW, "4 waves");
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 16, TN = WTN / 16;
+  constexpr bool AK = LAYOUT != LAY_TN;  // A stored k-contiguous
+  constexpr bool BK = LAYOUT == LAY_NT;  // B stored k-contiguous
+  constexpr int A_EL = BM * LBK, B_EL = BN * LBK;
+  constexpr int STAGE = A_EL + B_EL;  // elements
+  using ADma = typename std::conditional<AK, KDma<BM, false>, NDma<BM>>::type;
+  using BDma = typename std::conditional<BK, KDma<BN, KCAT>, NDma<BN>>::type;
+  constexpr int LOADS = ADma::PER_WAVE + BDma::PER_WAVE;  // DMA ops per wave per slab
+  static_assert(STAGES >= 2 && LOADS * STAGES < 64, "pipeline depth");
+
+  // epilogue staging: the finished tile goes through LDS (the ring is idle
+  // by then) and leaves as 16-byte chunks of consecutive rows
+  constexpr int LDS_CAP = 160 * 1024 / OCC;
+  constexpr int OES = EPI == EPI_STORE_F32 ? 4 : 2;  // output element bytes
+  constexpr int SROW = BN * OES + 16;               // staged row bytes (16-byte pad)
+  constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32) && BM * SROW <= LDS_CAP;
+  constexpr int SR3 = BN * 2 + 16;
+  constexpr bool STAGED3 = EPI == EPI_GELU_BWD && 2 * BM * SR3 <= LDS_CAP;
+  static_assert(EPI != EPI_GELU_BWD || STAGED3, "GELU backward needs its staged epilogue");
+  constexpr int RING_B = STAGES * STAGE * 2;
+  constexpr int STG_B = STAGED ? BM * SROW : (STAGED3 ? 2 * BM * SR3 : 0);
+  static_assert(RING_B <= LDS_CAP && STG_B <= LDS_CAP, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[RING_B > STG_B ? RING_B : STG_B];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int M = p.M, N = p.N;
+  const int nk = p.K / LBK;
+  int tm, tn;
+  tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint16_t *Ag = static_cast<const uint16_t *>(p.A);
+  const uint16_t *Bg = static_cast<const uint16_t *>(p.B);
+  if constexpr (LAYOUT == LAY_TN) {
+    // split-K: grid row z takes K rows [z K, (z+1) K) and writes its own partial
+    const int z = blockIdx.y;
+    Ag += (int64_t)z * p.K * p.lda;
+    Bg += (int64_t)z * p.K * p.ldb;
+    p.C = static_cast<float *>(p.C) + (int64_t)z * p.zstride;
+  }
+  // wave-uniform slab bases: k-type operands advance LBK elements per slab,
+  // m/n-type ones LBK rows
+  const uint16_t *Ab = AK ? Ag + (int64_t)m0 * p.lda : Ag + m0;
+  const uint16_t *Bb = BK ? Bg + (int64_t)n0 * p.ldb : Bg + n0;
+  const uint16_t *B2b = KCAT ? static_cast<const uint16_t *>(p.B2) + (int64_t)n0 * p.ldb2 : nullptr;
+  const int64_t astep = AK ? LBK : (int64_t)LBK * p.lda;
+  const int64_t bstep = BK ? LBK : (int64_t)LBK * p.ldb;
+
+  ADma da;
+  BDma db;
+  if constexpr (AK) da.init(p.lda, 0, m0, M, wave, lane);
+  else da.init(p.lda, m0, M, wave, lane);
+  if constexpr (BK) db.init(p.ldb, p.ldb2, n0, N, wave, lane);
+  else db.init(p.ldb, n0, N, wave, lane);
+
+  const uint32_t sbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 const void *)smem);
+  auto issue = [&](int kt, int stage) {
+    const uint32_t base = sbase + stage * (STAGE * 2);
+    if constexpr (AK) da.issue(Ab + kt * astep, false, base, wave);
+    else da.issue(Ab + kt * astep, base, wave);
+    if constexpr (BK) {
+      const int k0 = kt * LBK;
+      const bool second = KCAT && k0 >= p.K1;
+      db.issue(second ? B2b + (k0 - p.K1) : Bb + k0, second, base + A_EL * 2, wave);
+    } else {
+      db.issue(Bb + kt * bstep, base + A_EL * 2, wave);
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+
+  FragAddr<AK, BM, WTM> fa;
+  FragAddr<BK, BN, WTN> fb;
+  fa.init(0, wm * WTM, lane);
+  fb.init(A_EL * 2, wn * WTN, lane);
+  struct Frags {
+    uint4 a[TM];
+    uint4 b[TN];
+  };
+  auto load_chunk = [&](Frags &F, int stage, int kc) {
+    const char *st = smem + stage * (STAGE * 2);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) F.a[i] = fa.read(st, kc, i);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) F.b[j] = fb.read(st, kc, j);
+  };
+  constexpr int N_DS = TM * (AK ? 1 : 2) + TN * (BK ? 1 : 2);
+  constexpr int N_MFMA = TM * TN;
+  auto mma = [&](const Frags &F) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(F.b[j], F.a[i], acc[i][j]);
+  };
+  // interleave one LDS read after every few MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int q = 0; q < N_DS; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, N_MFMA / N_DS > 0 ? N_MFMA / N_DS : 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   // DS read
+    }
+  };
+  // first half of slab kt: MFMAs on chunk 0 (F0) while chunk 1 is read into F1
+  auto half0 = [&](int kt, Frags &F0, Frags &F1) {
+    load_chunk(F1, kt % STAGES, 1);
+    mma(F0);
+    interleave();
+  };
+  // second half of slab kt < nk-1: wait for slab kt+1, barrier (every wave
+  // has read both chunks of slab kt), refill slab kt's stage with slab
+  // kt+STAGES, MFMAs on chunk 1 while chunk 0 of slab kt+1 is read into F0
+  auto half1 = [&](int kt, Frags &F1, Frags &F0) {
+    if (kt + STAGES - 1 < nk) wait_vmcnt<LOADS * (STAGES - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    if (kt + STAGES < nk) issue(kt + STAGES, kt % STAGES);
+    load_chunk(F0, (kt + 1) % STAGES, 0);
+    mma(F1);
+    interleave();
+  };
+
+#pragma unroll
+  for (int s = 0; s < STAGES; ++s)
+    if (s < nk) issue(s, s);
+  if (nk >= STAGES) wait_vmcnt<LOADS * (STAGES - 1)>();
+  else wait_vmcnt<0>();
+  __syncthreads();
+  Frags F0, F1;
+  load_chunk(F0, 0, 0);
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    half0(kt, F0, F1);
+    half1(kt, F1, F0);
+  }
+  half0(nk - 1, F0, F1);
+  mma(F1);
+
+  // ---- epilogue: lane holds C[row][col .. col+3] of every 16x16 tile
+  const int g = lane >> 4, l16 = lane & 15;
+  if constexpr (STAGED) {
+    using OutT = typename std::conditional<EPI == EPI_STORE_F32, float, uint16_t>::type;
+    constexpr int CPR = BN * OES / 16;  // 16-byte chunks per tile row
+    float bv[TN][4];
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 16 + g * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) bv[j][r] = 0.f;
+      if (p.bias != nullptr && col < N) {
+        if constexpr (EPI == EPI_STORE_F32) load4(static_cast<const float *>(p.bias) + col, bv[j]);
+        else load4(static_cast<const uint16_t *>(p.bias) + col, bv[j]);
+      }
+    }
+    __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        float v[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][j][r] + bv[j][r];
+          if constexpr (EPI == EPI_GELU) v[r] = gelu_f(v[r]);
+        }
+        char *dst = smem + (wm * WTM + i * 16 + l16) * SROW + (wn * WTN + j * 16 + g * 4) * OES;
+        store4(reinterpret_cast<OutT *>(dst), v);
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+      const int rl = c / CPR, cc = c % CPR;
+      const int row = m0 + rl, col = n0 + cc * (16 / OES);
+      if (row < M && col < N)
+        store16_wt(static_cast<OutT *>(p.C) + (int64_t)row * p.ldc + col, smem + rl * SROW + cc * 16);
+    }
+    return;
+  }
+  if constexpr (STAGED3) {
+    // GELU backward: dH comes into LDS by coalesced 16-byte loads, then dZ
+    // and H are computed from the accumulators and dH one tile at a time,
+    // written to LDS and stored as whole row chunks (reading dH element by
+    // element between stores would wait on every store before it)
+    constexpr int CPR = BN * 2 / 16;
+    char *dhs = smem;
+    char *out = smem + BM * SR3;
+    if (p.bias != nullptr) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wn * WTN + j * 16 + g * 4;
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (col < N) load4(static_cast<const uint16_t *>(p.bias) + col, bv);
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += bv[r];
+      }
+    }
+    __syncthreads();  // every wave is done reading the ring
+    for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+      const int rl = c / CPR, cc = c % CPR;
+      const int row = m0 + rl, col = n0 + cc * 8;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (row < M && col < N)
+        v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
+      *reinterpret_cast<uint4 *>(dhs + rl * SR3 + cc * 16) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int off = (wm * WTM + i * 16 + l16) * SR3 + (wn * WTN + j * 16 + g * 4) * 2;
+          float dh[4], o[4];
+          load4(reinterpret_cast<const uint16_t *>(dhs + off), dh);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float z = acc[i][j][r];
+            o[r] = which == 0 ? dh[r] * gelu_grad_f(z) : gelu_f(z);
+          }
+          store4(reinterpret_cast<uint16_t *>(out + off), o);
+        }
+      }
+      __syncthreads();
+      void *C = which == 0 ? p.C : p.C2;  // dZ -> C, H -> C2
+      const int64_t ldc = which == 0 ? p.ldc : p.ldc2;
+      for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+        const int rl = c / CPR, cc = c % CPR;
+        const int row = m0 + rl, col = n0 + cc * 8;
+        if (row < M && col < N)
+          store16_wt(static_cast<uint16_t *>(C) + (int64_t)row * ldc + col, out + rl * SR3 + cc * 16);
+      }
+      __syncthreads();
+    }
+    return;
+  }
+  // direct stores (fp32 tiles too large to stage)
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int row = m0 + wm * WTM + i * 16 + l16;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int col = n0 + wn * WTN + j * 16 + g * 4;
+      if (row >= M || col >= N) continue;
+      float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+      const float u[4] = {0.f, 0.f, 0.f, 0.f};
+      epilogue4<uint16_t, EPI>(p, row, col, v, u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- host side
+template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT>
+static hipError_t run(const GemmArgs &a, hipStream_t s) {
+  GemmParams p;
+  p.A = a.A; p.lda = a.lda;
+  p.B = a.B; p.ldb = a.ldb;
+  p.B2 = a.B2; p.ldb2 = a.ldb2;
+  p.bias = a.bias;
+  p.D = a.D; p.ldd = a.ldd;
+  p.C = a.C; p.ldc = a.ldc;
+  p.C2 = a.C2; p.ldc2 = a.ldc2;
+  p.C3 = a.C3; p.ldc3 = a.ldc3;
+  p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K; p.K1 = (int)a.K1;
+  p.tiles_m = (int)((a.M + BM - 1) / BM);
+  p.tiles_n = (int)((a.N + BN - 1) / BN);
+  p.zstride = a.zstride;
+  hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT>),
+                     dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)a.splits), dim3(NW * 64), 0, s, p);
+  return hipGetLastError();
+}
+
+static int64_t cus() {
+  thread_local int cached_dev = -1, cached_n = 0;
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev == cached_dev) return cached_n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  cached_dev = dev;
+  cached_n = n;
+  return n;
+}
+
+// 256 x 256 tiles (one workgroup per CU) when they come in whole rounds over
+// the CUs; otherwise 128 x 128 tiles, two workgroups per CU.
+template <int LAYOUT, int EPI, bool KCAT>
+static hipError_t pick(const GemmArgs &a, hipStream_t s) {
+  const int64_t n = cus();
+  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
+  constexpr bool BIG_OK = EPI == EPI_STORE || EPI == EPI_STORE_F32;
+  if constexpr (BIG_OK) {
+    if (t256 >= n && t256 % n == 0) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
+  }
+  return run<128, 128, 2, 2, 2, 2, LAYOUT, EPI, KCAT>(a, s);
+}
+
+}  // namespace k64
+
+hipError_t launch_gemm_k64(const GemmArgs &a, hipStream_t s) {
+  using namespace k64;
+  if (a.dtype != DT_BF16 || a.dual || a.K <= 0 || a.K % LBK != 0) return hipErrorNotSupported;
+  if (a.kcat && (a.K1 % LBK != 0 || a.layout != LAY_NT)) return hipErrorNotSupported;
+  if (a.M < 8 || a.N < 8) return hipErrorNotSupported;
+  // the DMA offsets are 32-bit (up to 256 rows of a k-contiguous operand or
+  // 64 rows of an m/n-contiguous one, relative to the slab base)
+  const int64_t ld_max = std::max(a.lda, std::max(a.ldb, a.kcat ? a.ldb2 : (int64_t)0));
+  if (ld_max * 2 * 256 >= ((int64_t)1 << 32)) return hipErrorNotSupported;
+  // small products stay on the other kernels (more, smaller tiles)
+  if (((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits < 128) return hipErrorNotSupported;
+  if (a.splits > 1 && (a.layout != LAY_TN || a.epi != EPI_STORE_F32)) return hipErrorInvalidValue;
+  switch (a.layout) {
+    case LAY_NN:
+      switch (a.epi) {
+        case EPI_STORE: return pick<LAY_NN, EPI_STORE, false>(a, s);
+        case EPI_STORE_F32: return pick<LAY_NN, EPI_STORE_F32, false>(a, s);
+        case EPI_GELU: return pick<LAY_NN, EPI_GELU, false>(a, s);
+        case EPI_GELU_BWD: return pick<LAY_NN, EPI_GELU_BWD, false>(a, s);
+        default: return hipErrorNotSupported;
+      }
+    case LAY_NT:
+      if (a.kcat) {
+        if (a.epi == EPI_STORE_F32) return pick<LAY_NT, EPI_STORE_F32, true>(a, s);
+        return hipErrorNotSupported;
+      }
+      if (a.epi == EPI_STORE) return pick<LAY_NT, EPI_STORE, false>(a, s);
+      if (a.epi == EPI_STORE_F32) return pick<LAY_NT, EPI_STORE_F32, false>(a, s);
+      return hipErrorNotSupported;
+    case LAY_TN:
+      if (a.epi != EPI_STORE_F32) return hipErrorNotSupported;
+      return pick<LAY_TN, EPI_STORE_F32, false>(a, s);
+  }
+  return hipErrorNotSupported;
+}
+
+}  // namespace tpcol

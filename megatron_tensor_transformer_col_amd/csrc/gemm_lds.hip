@@ -1,6 +1,6 @@
 // bf16 MFMA GEMM for gfx950 fed by direct HBM -> LDS DMA.
 //
-//   C[M x N] = A[M x K] . B[K x N]   (fp32 accumulate, K a multiple of 64)
+//   C[M x N] = A[M x K] . B[K x N]   (fp32 accumulate, K a multiple of 32)
 //
 // Same operand layouts and fused epilogues as the general kernel (gemm.hip);
 // what changes is the data path, built for CDNA4:

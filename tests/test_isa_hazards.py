@@ -14,7 +14,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "megatron_tensor_transformer_col_amd", "csrc")
-SOURCES = ["attention.hip", "attn_bwd.hip", "gemv.hip", "gemm_lds.hip"]
+SOURCES = ["attention.hip", "attn_bwd.hip", "gemv.hip", "gemm_lds.hip", "gemm_k64.hip"]
 WAIT_STATES = 5
 
 pytestmark = pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
@@ -68,8 +68,8 @@ def _hipcc():
 def test_no_valu_sgpr_hazard_before_lds_dma(src, tmp_path):
     flags = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops"]
-    if src == "attention.hip":
-        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    from megatron_tensor_transformer_col_amd import _build
+    flags += _build.EXTRA_FLAGS.get(src, [])
     out = tmp_path / (src + ".s")
     r = subprocess.run([_hipcc(), *flags, "-S", "--cuda-device-only", "-o", str(out), os.path.join(CSRC, src)],
                        capture_output=True, text=True)
