@@ -161,32 +161,47 @@ def _stream(stream, ref):
 
 
 class _WorkspaceCache:
-    """Per-device scratch buffers owned by the binding, one pool for the
-    linear calls' decode path and one for attention / backward."""
+    """Scratch buffers owned by the binding for calls made without ws=, one per
+    (device, stream, zeroed): a call's workspace must not be used by another
+    call that can run at the same time, and calls on one stream are ordered.
+    A buffer that grows is replaced on the same stream, so torch's allocator
+    reuses the old block only after the work already queued there."""
 
     def __init__(self):
         self._bufs = {}
+        self._lock = threading.Lock()
 
-    def get(self, nbytes, device, zeroed):
+    def get(self, nbytes, device, stream, zeroed):
         if nbytes == 0:
             return None
         torch = _torch()
-        key = (str(device), zeroed)
-        buf = self._bufs.get(key)
-        if buf is None or buf.numel() < nbytes:
-            alloc = torch.zeros if zeroed else torch.empty
-            buf = alloc(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
-            self._bufs[key] = buf
-        return buf
+        key = (str(device), int(stream or 0), zeroed)
+        with self._lock:
+            buf = self._bufs.get(key)
+            if buf is None or buf.numel() < nbytes:
+                alloc = torch.zeros if zeroed else torch.empty
+                s = torch.cuda.ExternalStream(stream, device=device) if stream else None
+                with torch.cuda.stream(s) if s is not None else _nullcontext():
+                    buf = alloc(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+                self._bufs[key] = buf
+            return buf
 
 
 _ws_cache = _WorkspaceCache()
 
 
-def _workspace(ws, nbytes, device, zeroed):
+class _nullcontext:
+    def __enter__(self):
+        return None
+
+    def __exit__(self, *exc):
+        return False
+
+
+def _workspace(ws, nbytes, device, zeroed, stream=None):
     if ws is not None:
         return ws.data_ptr(), ws.numel() * ws.element_size()
-    buf = _ws_cache.get(nbytes, device, zeroed)
+    buf = _ws_cache.get(nbytes, device, stream, zeroed)
     return (None, 0) if buf is None else (buf.data_ptr(), buf.numel())
 
 
@@ -220,7 +235,8 @@ def tp_col_linear_gelu(X, W, H, act="gelu", Wup=None, bias=None, ws=None, stream
     pu, _, _, ldu = _mat(Wup, "Wup")
     ph, _, _, ldh = _mat(H, "H")
     need = tp_col_linear_gelu_workspace(dt, a, M, K, Ni)
-    pws, nws = _workspace(ws, need, X.device, zeroed=True)
+    st = _stream(stream, X)
+    pws, nws = _workspace(ws, need, X.device, zeroed=True, stream=st)
     _check("tp_col_linear_gelu", lib().tp_col_linear_gelu(
         dt, a, M, K, Ni, px, ldx, pw, ldw, pu, ldu, _ptr(bias), ph, ldh, pws, nws,
         _stream(stream, X)))
@@ -234,7 +250,8 @@ def tp_row_linear_partial(Xi, Wi, P, ws=None, stream=None):
     pw, _, N, ldw = _mat(Wi, "Wi")
     pp, _, _, ldp = _mat(P, "P")
     need = tp_row_linear_partial_workspace(dt, M, Ki, N)
-    pws, nws = _workspace(ws, need, Xi.device, zeroed=True)
+    st = _stream(stream, Xi)
+    pws, nws = _workspace(ws, need, Xi.device, zeroed=True, stream=st)
     _check("tp_row_linear_partial", lib().tp_row_linear_partial(
         dt, M, Ki, N, px, ldx, pw, ldw, pp, ldp, pws, nws, _stream(stream, Xi)))
     return P
@@ -249,7 +266,8 @@ def tp_attn_heads_shard(X, Wqkv, Wo, P, b, s, heads_local, d=128, causal=True, w
     po, _, _, ldo = _mat(Wo, "Wo")
     pp, _, _, ldp = _mat(P, "P")
     need = tp_attn_heads_shard_workspace(dt, b, s, heads_local, d)
-    pws, nws = _workspace(ws, need, X.device, zeroed=False)
+    st = _stream(stream, X)
+    pws, nws = _workspace(ws, need, X.device, zeroed=False, stream=st)
     _check("tp_attn_heads_shard", lib().tp_attn_heads_shard(
         dt, b, s, h, heads_local, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo, pp, ldp,
         pws, nws, _stream(stream, X)))
@@ -267,7 +285,8 @@ def tp_attn_gqa_shard(X, Wqkv, Wo, P, b, s, heads_local, kv_heads_local, d=128, 
     po, _, _, ldo = _mat(Wo, "Wo")
     pp, _, _, ldp = _mat(P, "P")
     need = tp_attn_gqa_shard_workspace(dt, b, s, heads_local, kv_heads_local, d)
-    pws, nws = _workspace(ws, need, X.device, zeroed=False)
+    st = _stream(stream, X)
+    pws, nws = _workspace(ws, need, X.device, zeroed=False, stream=st)
     _check("tp_attn_gqa_shard", lib().tp_attn_gqa_shard(
         dt, b, s, h, heads_local, kv_heads_local, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo,
         pp, ldp, pws, nws, _stream(stream, X)))
@@ -296,7 +315,8 @@ def tp_attn_shard_backward(X, Wqkv, Wo, dY, fwd_ws, dWqkv, dWo, dXi, b, s, heads
         if not t.is_contiguous():
             raise ValueError(f"{name} must be dense")
     need = tp_attn_shard_backward_workspace(dt, b, s, heads_local, kvl, d)
-    pws, nws = _workspace(ws, need, X.device, zeroed=False)
+    st = _stream(stream, X)
+    pws, nws = _workspace(ws, need, X.device, zeroed=False, stream=st)
     _check("tp_attn_shard_backward", lib().tp_attn_shard_backward(
         dt, b, s, h, heads_local, kvl, d, 1 if causal else 0, px, ldx, pq, ldq, po, ldo, py, ldy,
         fwd_ws.data_ptr(), fwd_ws.numel() * fwd_ws.element_size(), dWqkv.data_ptr(), dWo.data_ptr(), pd, lddx,
@@ -389,7 +409,8 @@ def tp_mlp_shard_backward(X, W1, W2, dY, dW1, dW2, dXi, act="gelu", Wup=None, b1
     pdy, _, _, lddy = _mat(dY, "dY")
     pdx, _, _, lddx = _mat(dXi, "dXi")
     need = tp_mlp_shard_backward_workspace(dt, a, M, Ni)
-    pws, nws = _workspace(ws, need, X.device, zeroed=False)
+    st = _stream(stream, X)
+    pws, nws = _workspace(ws, need, X.device, zeroed=False, stream=st)
     _check("tp_mlp_shard_backward", lib().tp_mlp_shard_backward(
         dt, a, M, K, Ni, px, ldx, pw1, ldw1, pu, ldu, _ptr(b1), pw2, ldw2, pdy, lddy,
         _ptr(dW1), _ptr(dWup), _ptr(dW2), _ptr(db1), pdx, lddx, pws, nws, _stream(stream, X)))

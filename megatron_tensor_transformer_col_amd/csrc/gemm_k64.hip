@@ -251,12 +251,24 @@ gemm_k64_kernel(GemmParams pin) {
 #pragma unroll
       for (int j = 0; j < TN; ++j) acc[i][j] = mfma16(F.b[j], F.a[i], acc[i][j]);
   };
-  // interleave one LDS read after every few MFMAs
+  // interleave the next chunk's LDS reads with this chunk's MFMAs.  Two
+  // workgroups per CU: the reads go out early (one after each of the first
+  // MFMAs) so that they have landed before the chunk ends; one workgroup per
+  // CU: spread evenly.
   auto interleave = [&]() {
+    if constexpr (OCC > 1 && N_MFMA > N_DS) {
 #pragma unroll
-    for (int q = 0; q < N_DS; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, N_MFMA / N_DS > 0 ? N_MFMA / N_DS : 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                   // DS read
+      for (int q = 0; q < N_DS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, N_MFMA - N_DS, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < N_DS; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, N_MFMA / N_DS > 0 ? N_MFMA / N_DS : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
   };
   // first half of slab kt: MFMAs on chunk 0 (F0) while chunk 1 is read into F1
