@@ -20,7 +20,8 @@ import threading
 
 __all__ = [
     "TpError", "lib", "library_path", "TP_F32", "TP_BF16", "TP_ACT_NONE", "TP_ACT_GELU_ERF",
-    "TP_ACT_SWIGLU", "tp_col_linear_gelu", "tp_row_linear_partial", "tp_attn_heads_shard",
+    "TP_ACT_SWIGLU", "tp_col_linear_gelu", "tp_col_linear_gelu_noalloc", "tp_row_linear_partial",
+    "tp_attn_heads_shard",
     "tp_attn_gqa_shard", "tp_attn_gqa_shard_workspace", "tp_attn_shard_backward",
     "tp_attn_shard_backward_workspace", "tp_shard_reduce_scatter_layernorm",
     "tp_vocab_ce_shard_stats", "tp_vocab_ce_lse", "tp_vocab_ce_shard_loss", "tp_vocab_ce_total",
@@ -41,6 +42,8 @@ _SIGS = {
     "tp_col_linear_gelu": (_int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                   _vp, _vp, _i64, _vp, _sz, _vp]),
     "tp_col_linear_gelu_workspace": (_sz, [_int, _int, _i64, _i64, _i64]),
+    "tp_col_linear_gelu_noalloc": (_int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                          _vp, _vp, _i64, _vp]),
     "tp_row_linear_partial": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                      _vp, _sz, _vp]),
     "tp_row_linear_partial_workspace": (_sz, [_int, _i64, _i64, _i64]),
@@ -240,6 +243,19 @@ def tp_col_linear_gelu(X, W, H, act="gelu", Wup=None, bias=None, ws=None, stream
     _check("tp_col_linear_gelu", lib().tp_col_linear_gelu(
         dt, a, M, K, Ni, px, ldx, pw, ldw, pu, ldu, _ptr(bias), ph, ldh, pws, nws,
         _stream(stream, X)))
+    return H
+
+
+def tp_col_linear_gelu_noalloc(X, W, H, act="gelu", Wup=None, bias=None, stream=None):
+    """tp_col_linear_gelu without a workspace (the library's static scratch)."""
+    dt = _dtype_code(X)
+    a = _ACTS[act] if isinstance(act, str) else int(act)
+    px, M, K, ldx = _mat(X, "X")
+    pw, _, Ni, ldw = _mat(W, "W")
+    pu, _, _, ldu = _mat(Wup, "Wup")
+    ph, _, _, ldh = _mat(H, "H")
+    _check("tp_col_linear_gelu_noalloc", lib().tp_col_linear_gelu_noalloc(
+        dt, a, M, K, Ni, px, ldx, pw, ldw, pu, ldu, _ptr(bias), ph, ldh, _stream(stream, X)))
     return H
 
 

@@ -402,14 +402,18 @@ size_t tp_mlp_shard_backward_workspace(int dtype, int act, int64_t M, int64_t Ni
   return bwd_ws(dtype, act, M, Ni).total;
 }
 
-int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
-                       int64_t ldx, const void *W, int64_t ldw, const void *Wup, int64_t ldwu,
-                       const void *bias, void *H, int64_t ldh, void *ws, size_t ws_bytes,
-                       void *stream) {
+}  // extern "C"
+
+namespace {
+// tp_col_linear_gelu and its allocation-free variant (noalloc: the decode
+// path's split-K scratch is the library's static array, no ws)
+int col_linear_impl(const char *fn, int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
+                    int64_t ldx, const void *W, int64_t ldw, const void *Wup, int64_t ldwu, const void *bias,
+                    void *H, int64_t ldh, void *ws, size_t ws_bytes, void *stream, bool noalloc) {
   if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
   if (act != TP_ACT_NONE && act != TP_ACT_GELU_ERF && act != TP_ACT_SWIGLU)
     return fail(TP_ERR_ARG, "activation %d", act);
-  TRY(check_dims({M, K, Ni}, "tp_col_linear_gelu"));
+  TRY(check_dims({M, K, Ni}, fn));
   if (K < 1 || Ni < 1) return fail(TP_ERR_SHAPE, "K and Ni must be >= 1");
   const size_t e = esize(dtype);
   TRY(check_mat(X, M, K, ldx, e, "X"));
@@ -427,17 +431,25 @@ int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni, con
   hipStream_t s = static_cast<hipStream_t>(stream);
 
   if (act != TP_ACT_SWIGLU && use_gemv(dtype, M) && Ni <= gemv_max_n() && gemv_fits(ldx, ldw)) {
-    const size_t need = gemv_workspace(K, Ni);
-    if (need > 0 && (ws == nullptr || ws_bytes < need))
-      return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);
-    if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
-      return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
     GemvArgs g;
     g.dtype = DT_BF16;
     g.epi = act == TP_ACT_GELU_ERF ? EPI_GELU : EPI_STORE;
     g.M = M; g.K = K; g.N = Ni;
     g.X = X; g.ldx = ldx; g.W = W; g.ldw = ldw; g.bias = bias;
-    g.Y = H; g.ldy = ldh; g.ws = ws; g.ws_bytes = ws_bytes;
+    g.Y = H; g.ldy = ldh;
+    if (noalloc) {
+      if (!gemv_noalloc_fits(K, Ni))
+        return fail(TP_ERR_SHAPE, "%s: decode partials of K %lld x Ni %lld exceed the %zu-byte static scratch", fn,
+                    (long long)K, (long long)Ni, gemv_noalloc_max_bytes());
+      TRY(hip_status(launch_gemv_noalloc(g, s), "gemv"));
+      return ok();
+    }
+    const size_t need = gemv_workspace(K, Ni);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+      return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+      return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+    g.ws = ws; g.ws_bytes = ws_bytes;
     TRY(hip_status(launch_gemv(g, s), "gemv"));
     return ok();
   }
@@ -459,6 +471,25 @@ int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni, con
   }
   TRY(hip_status(launch_gemm(a, s), "column GEMM"));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_col_linear_gelu(int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
+                       int64_t ldx, const void *W, int64_t ldw, const void *Wup, int64_t ldwu,
+                       const void *bias, void *H, int64_t ldh, void *ws, size_t ws_bytes,
+                       void *stream) {
+  return col_linear_impl("tp_col_linear_gelu", dtype, act, M, K, Ni, X, ldx, W, ldw, Wup, ldwu, bias, H, ldh,
+                         ws, ws_bytes, stream, false);
+}
+
+int tp_col_linear_gelu_noalloc(int dtype, int act, int64_t M, int64_t K, int64_t Ni, const void *X,
+                               int64_t ldx, const void *W, int64_t ldw, const void *Wup, int64_t ldwu,
+                               const void *bias, void *H, int64_t ldh, void *stream) {
+  return col_linear_impl("tp_col_linear_gelu_noalloc", dtype, act, M, K, Ni, X, ldx, W, ldw, Wup, ldwu, bias, H,
+                         ldh, nullptr, 0, stream, true);
 }
 
 int tp_row_linear_partial(int dtype, int64_t M, int64_t Ki, int64_t N, const void *Xi, int64_t ldx,

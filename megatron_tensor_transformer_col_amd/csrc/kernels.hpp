@@ -66,6 +66,12 @@ size_t gemv_workspace(int64_t K, int64_t N);
 int64_t gemv_max_n();  // widest N the split-K decode path accepts
 bool gemv_fits(int64_t ldx, int64_t ldw);  // row strides the decode path's 32-bit offsets cover
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
+// The same with the split-K partials and arrival counters in the library's
+// static scratch (no workspace; one kernel).  gemv_noalloc_fits: the shape's
+// partials fit that scratch (gemv_noalloc_max_bytes()).
+hipError_t launch_gemv_noalloc(const GemvArgs &a, hipStream_t s);
+bool gemv_noalloc_fits(int64_t K, int64_t N);
+size_t gemv_noalloc_max_bytes();
 
 // Y = sum_i P_i (+ bias), float32 partials, float32 or bf16 output.
 hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *parts,
