@@ -152,6 +152,32 @@ def per_call_ms(torch, fn, iters):
     return t[len(t) // 2], t[0]
 
 
+def device_peaks():
+    """The denominators measured on this machine: compute units and maximum engine
+    clock of the GPU agent (rocminfo), and the dense bf16 MFMA peak they give
+    (4096 flop per clock per CU: 4 SIMDs x 1024), beside the published figures
+    the fractions use."""
+    import subprocess
+    cus = mhz = None
+    try:
+        txt = subprocess.run(["rocminfo"], capture_output=True, text=True, timeout=60).stdout
+        for block in txt.split("*******"):
+            if "gfx950" in block and "Compute Unit:" in block:
+                for line in block.splitlines():
+                    if line.strip().startswith("Compute Unit:"):
+                        cus = int(line.split(":")[1])
+                    if line.strip().startswith("Max Clock Freq. (MHz):"):
+                        mhz = int(line.split(":")[1])
+                break
+    except Exception:
+        pass
+    out = {"source": "rocminfo", "compute_units": cus, "max_sclk_mhz": mhz,
+           "spec_bf16_tflops": PEAK_BF16_TFLOPS, "spec_hbm_gbs": PEAK_HBM_GBS}
+    if cus and mhz:
+        out["derived_bf16_tflops"] = round(cus * 4096 * mhz * 1e6 / 1e12, 1)
+    return out
+
+
 def copy_gbs(torch):
     """Measured HBM reference: a 1 GiB device-to-device copy (reads 1 GiB,
     writes 1 GiB; 4x the 256 MiB last-level cache), bytes moved / time."""
@@ -208,6 +234,42 @@ def headline(torch, tp, synth, steps, warmup):
                    "tokens": hl.T, "h": hl.h, "ffn": hl.W.ffn, "n_shards": hl.n,
                    "activation": "gelu_erf", "timing": "9 launches per step, enqueued back to back"},
     }
+
+
+def other_rooflines(torch, tp):
+    """Roofline blocks of the largest workload's dominant kernel (the Llama
+    SwiGLU column dual GEMM, 481 GFLOP per launch) and of the decode GEMV
+    (one column GEMV of the 8-shard decode MLP: 58.7 MB of weights per call,
+    the 8 shards' weights rotated so that none is cache-resident), each timed
+    with HIP events over back-to-back launches on the launch stream."""
+    R = Rows(torch, tp)
+    out = {}
+    s = R.swiglu()
+    ms = back_to_back_ms(torch, lambda: R.swiglu_col(s), 10)
+    fl = 2 * s["flop_gemm"]
+    out["llama_swiglu_dual_gemm"] = {
+        "bound": "mfma", "kernel": "column dual GEMM + SwiGLU epilogue (8192 x 4096 x 2 x 3584)",
+        "achieved": round(fl / ms / 1e9, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(ms * 1e3, 2),
+        "flops_per_launch": fl, "traffic": None}
+    del s
+    s = R.decode()
+    it = [0]
+
+    def col(noalloc=False):
+        i = it[0] % s["n"]
+        it[0] += 1
+        f = tp.tp_col_linear_gelu_noalloc if noalloc else tp.tp_col_linear_gelu
+        f(s["x"], s["W1"][i], s["H"][i])
+    ms = back_to_back_ms(torch, col, 64)
+    ms_na = back_to_back_ms(torch, lambda: col(True), 64)
+    wb = s["w_bytes"]
+    out["decode_gemv"] = {
+        "bound": "hbm", "kernel": "decode column GEMV (split-K pass + finalize, 16 x 8192 x 3584, GELU)",
+        "achieved": round(wb / ms / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(wb / ms / 1e6 / PEAK_HBM_GBS, 4), "avg_call_us": round(ms * 1e3, 2),
+        "weight_bytes_per_call": wb, "noalloc_avg_call_us": round(ms_na * 1e3, 2), "traffic": None}
+    return out
 
 
 # --------------------------------------------------------------------------- other workloads
@@ -352,6 +414,12 @@ class Rows:
         s["bytes"] = float(T) * N * (4 * n + 4 + 4 + 2)
         return s
 
+    def cold_sets(self, make, nsets):
+        """nsets independent input sets (rotated per call so that each call's
+        inputs were last touched nsets - 1 calls earlier: with nsets x the set
+        size above the 256 MiB last-level cache, every call reads HBM)."""
+        return [make() for _ in range(nsets)]
+
     def sp_ln_step(self, s):
         rows = s["T"] // s["n"]
         for r in range(s["n"]):
@@ -467,6 +535,35 @@ def rows(torch, tp, steps, warmup):
                                                   "LayerNorm) per graph replay; bytes = partials + residual "
                                                   "read, fp32 sum + bf16 output written"}
     del s
+    # shard sum and sequence-parallel LayerNorm with their inputs out of the
+    # last-level cache: 3 input sets (3 x 160 MiB / 3 x 208 MiB) rotated
+    sets = R.cold_sets(lambda: {"P": [R.empty((8192, 1024), torch.float32).normal_() for _ in range(4)],
+                                "Y": R.empty((8192, 1024), torch.float32)}, 3)
+    it = [0]
+
+    def sum_cold():
+        c = sets[it[0] % 3]
+        it[0] += 1
+        tp.tp_shard_sum(c["P"], c["Y"])
+    ms_s = back_to_back_ms(torch, sum_cold, 30)
+    bsum = 5.0 * 8192 * 1024 * 4
+    out["shard_sum_cold"] = {"ms": ms_s, "bytes": bsum, "gbs": bsum / ms_s / 1e6,
+                             "frac_hbm_peak": bsum / ms_s / 1e6 / PEAK_HBM_GBS,
+                             "note": "Y = sum of 4 fp32 partials [8192 x 1024], 3 input sets rotated (480 MiB > "
+                                     "the 256 MiB last-level cache): reads and writes reach HBM"}
+    del sets
+    sl = [R.sp_ln() for _ in range(3)]
+    it = [0]
+
+    def spln_cold():
+        R.sp_ln_step(sl[it[0] % 3])
+        it[0] += 1
+    ms_l2 = back_to_back_ms(torch, spln_cold, 15)
+    out["sp_reduce_scatter_layernorm_cold"] = {
+        "ms": ms_l2, "bytes": sl[0]["bytes"], "gbs": sl[0]["bytes"] / ms_l2 / 1e6,
+        "frac_hbm_peak": sl[0]["bytes"] / ms_l2 / 1e6 / PEAK_HBM_GBS,
+        "note": "as sp_reduce_scatter_layernorm, 3 input sets rotated (~650 MiB): HBM-resident inputs"}
+    del sl
     s = R.vocab_ce()
     gc = graph_of(torch, lambda: R.vocab_ce_step(s))
     ms_c, _ = timed(torch, lambda kt: gc.replay(), s_ms, w_ms)
@@ -522,12 +619,28 @@ def run_op(torch, tp, synth, name, iters):
         elif name == "c7_spln":
             s = R.sp_ln()
             fn = lambda: R.sp_ln_step(s)
+        elif name == "c7_spln_cold":
+            sl = [R.sp_ln() for _ in range(3)]
+            it = [0]
+
+            def fn():
+                R.sp_ln_step(sl[it[0] % 3])
+                it[0] += 1
+        elif name == "c2_sum_cold":
+            sets = [{"P": [R.empty((8192, 1024), torch.float32).normal_() for _ in range(4)],
+                     "Y": R.empty((8192, 1024), torch.float32)} for _ in range(3)]
+            it = [0]
+
+            def fn():
+                c = sets[it[0] % 3]
+                it[0] += 1
+                tp.tp_shard_sum(c["P"], c["Y"])
         elif name == "c8_ce":
             s = R.vocab_ce()
             fn = lambda: R.vocab_ce_step(s)
         elif name.startswith("c5_"):
             s = R.decode()
-            k = {"c5_col": 0, "c5_row": 1}[name]
+            k = {"c5_col": 0, "c5_row": 1, "c5_col_noalloc": 2}[name]
             it = [0]
 
             def fn():
@@ -535,6 +648,8 @@ def run_op(torch, tp, synth, name, iters):
                 it[0] += 1
                 if k == 0:
                     tp.tp_col_linear_gelu(s["x"], s["W1"][i], s["H"][i])
+                elif k == 2:
+                    tp.tp_col_linear_gelu_noalloc(s["x"], s["W1"][i], s["H"][i])
                 else:
                     tp.tp_row_linear_partial(s["H"][i], s["W2"][i], s["P"][i])
         else:
@@ -556,7 +671,7 @@ def run_op(torch, tp, synth, name, iters):
 
 # --------------------------------------------------------------------------- HBM traffic
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_col_gelu_gpt2m_shard.md")
-TRAFFIC_SOURCES = ["gemm_lds.hip", "gemm_common.hpp", "device_common.hpp", "lds_dma.hpp"]
+TRAFFIC_SOURCES = ["gemm_k64.hip", "gemm_common.hpp", "device_common.hpp", "lds_dma.hpp"]
 
 
 def col_gemm_traffic():
@@ -580,31 +695,120 @@ def col_gemm_traffic():
 
 
 # --------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(synth, seconds):
-    import oracle
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads():
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = os.cpu_count() or 1
+        return os.cpu_count() or 1
+
+
+def _time(fn, min_s):
+    """Wall seconds per call of fn, repeated until min_s have passed."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            return el / n, n
+
+
+def cpu_baseline(synth, seconds):
+    """The fp64 oracle (NumPy BLAS, as it stands) timed on this host's cores on
+    bounded samples of every workload, the unsharded computation each time.
+    `value` is the headline workload's (GPT-2-medium MLP, forward); `configs`
+    carries every workload, scaled from its sample to the full unsharded
+    algorithmic flops (rows are independent, and weight gradients are sums
+    over rows, so the work is linear in the sampled rows / batch elements /
+    column blocks).  Inputs are seeded float32 draws of each workload's
+    distributions; the oracle's cost does not depend on the values."""
+    import numpy as np
+    import oracle
+    from oracle import brute
+    rng = np.random.default_rng(0)
+    nrm = lambda shape, std: rng.standard_normal(shape, dtype=np.float32).astype(np.float64) * std
+    share = max(seconds / 6.0, 0.5)
+    out = {}
+
+    def rec(name, sec, flops_sample, flops_full, sample, calls):
+        out[name] = {"sec_per_call": round(sec, 4), "gflops": round(flops_sample / sec / 1e9, 2),
+                     "full_unsharded_gflop": round(flops_full / 1e9, 3),
+                     "est_full_sec": round(sec * flops_full / flops_sample, 3), "sample": sample, "calls": calls}
+
+    # C1 tiny fp32 MLP, T 32, h 128, ffn 512: whole forward and backward, and the loop version
+    w = synth.WORKLOADS["tiny_mlp_f32"]
+    d = synth.make_mlp_inputs(w.tokens, w.h, w.ffn, "f32", seed=w.seed, with_dy=True)
+    X, W1, W2, dY = d["X"].f64(), d["W1"].f64(), d["W2"].f64(), d["dY"].f64()
+    f1 = 2.0 * 2 * w.tokens * w.h * w.ffn
+    sec, n = _time(lambda: oracle.mlp_gelu(X, W1, W2), 0.2)
+    rec("tiny_mlp_f32_fwd", sec, f1, f1, "whole workload", n)
+    sec, n = _time(lambda: oracle.mlp_gelu_backward(X, W1, W2, dY), 0.2)
+    rec("tiny_mlp_f32_bwd", sec, 2 * f1, 2 * f1, "whole workload (dH, dW2, dW1, dX)", n)
+    Xl, W1l, W2l = X.tolist(), W1.tolist(), W2.tolist()
+    sec, n = _time(lambda: brute.mlp_gelu(Xl, W1l, W2l), 0.5)
+    rec("tiny_mlp_f32_fwd_brute", sec, f1, f1, "whole workload, pure-Python loops, one core", n)
+
+    # C2 GPT-2-medium MLP forward on 1024-row blocks (the headline)
     W = synth.WORKLOADS["gpt2m_mlp_bf16"]
     d = synth.make_mlp_inputs(W.tokens, W.h, W.ffn, "bf16", seed=W.seed)
     X, W1, W2 = d["X"].f64(), d["W1"].f64(), d["W2"].f64()
-    rows = 1024                       # token rows per oracle call (rows are independent)
-    flops = 2 * 2.0 * rows * W.h * W.ffn
-    t0 = time.perf_counter()
-    done, calls = 0.0, 0
-    while True:
-        r0 = (calls * rows) % W.tokens
+    rows = 1024
+    it = [0]
+
+    def c2():
+        r0 = (it[0] * rows) % W.tokens
+        it[0] += 1
         oracle.mlp_gelu(X[r0:r0 + rows], W1, W2)
-        calls += 1
-        done += flops
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    return {"value": done / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 oracle, unsharded GELU MLP (h 1024, ffn 4096) on {calls} x {rows} "
-                      f"token rows of the headline workload, {el:.1f} s"}
+    sec, n = _time(c2, max(2 * share, 2.0))
+    f2s, f2 = 2.0 * 2 * rows * W.h * W.ffn, 2.0 * 2 * W.tokens * W.h * W.ffn
+    rec("gpt2m_mlp_bf16_fwd", sec, f2s, f2, f"{rows} of {W.tokens} token rows per call", n)
+    head = out["gpt2m_mlp_bf16_fwd"]
+    del d, X, W1, W2
+
+    # C3 Llama SwiGLU MLP, forward and backward on 256 token rows, full weights
+    T3, h3, f3, r3 = 8192, 4096, 14336, 256
+    X, Wg, Wu, Wd, dY = nrm((r3, h3), 1.0), nrm((h3, f3), 0.02), nrm((h3, f3), 0.02), nrm((f3, h3), 0.02), nrm((r3, h3), 1.0)
+    g3 = 2.0 * h3 * f3
+    sec, n = _time(lambda: oracle.mlp_swiglu(X, Wg, Wu, Wd), share)
+    rec("llama_swiglu_bf16_fwd", sec, 3 * g3 * r3, 3 * g3 * T3, f"{r3} of {T3} token rows per call", n)
+    rb = r3 // 2
+    sec, n = _time(lambda: oracle.mlp_swiglu_backward(X[:rb], Wg, Wu, Wd, dY[:rb]), share)
+    rec("llama_swiglu_bf16_bwd", sec, 6 * g3 * rb, 6 * g3 * T3,
+        f"{rb} of {T3} token rows per call (dWg, dWu, dWd summed over those rows)", n)
+    del X, Wg, Wu, Wd, dY
+
+    # C4 MHA, b 4 x s 2048, h 4096, 32 heads of 128, causal: one batch element
+    s4, h4, H4, b4 = 2048, 4096, 32, 4
+    X = nrm((s4, h4), 1.0)
+    Wq, Wk, Wv, Wo = (nrm((h4, h4), 0.02) for _ in range(4))
+    f4 = 2.0 * s4 * h4 * 3 * h4 + 4.0 * 128 * s4 * (s4 + 1) / 2 * H4 + 2.0 * s4 * h4 * h4
+    sec, n = _time(lambda: oracle.mha(X, Wq, Wk, Wv, Wo, heads=H4, b=1, s=s4, causal=True), share)
+    rec("mha_heads_bf16_fwd", sec, f4, b4 * f4, f"batch element 1 of {b4} (the oracle forms the full score matrix)", n)
+    del X, Wq, Wk, Wv, Wo
+
+    # C5 decode MLP, 16 tokens, h 8192, ffn 28672: one shard's column block (3584) of W1 / row block of W2
+    h5, f5, n5 = 8192, 28672, 8
+    x, W1, W2 = nrm((16, h5), 1.0), nrm((h5, f5 // n5), 0.02), nrm((f5 // n5, h5), 0.02)
+    f5s = 2.0 * 2 * 16 * h5 * (f5 // n5)
+    sec, n = _time(lambda: oracle.mlp_gelu(x, W1, W2), share)
+    rec("decode_mlp_bf16_fwd", sec, f5s, n5 * f5s, f"column block 1 of {n5} of the ffn (GELU is column-separable)", n)
+    return {"value": round(head["gflops"] / 1e3, 4), "unit": "TFLOP/s", "cores": int(_blas_threads()),
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"fp64 oracle (NumPy BLAS), unsharded GELU MLP of the headline workload (h 1024, ffn 4096) "
+                      f"on {head['sample']}; per-workload samples in configs",
+            "configs": out}
 
 
 def main():
@@ -630,7 +834,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(hl["ms"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic", "config": hl["config"],
-        "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU epilogue (gemm_lds_kernel NN, 128x256 tile)",
+        "roofline": {"bound": "mfma", "kernel": "column GEMM + GELU epilogue (gemm_k64_kernel NN, 128x128 tiles, two workgroups per CU)",
                      "achieved": round(hl["col_tflops"], 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(hl["col_tflops"] / PEAK_BF16_TFLOPS, 4),
                      "traffic": col_gemm_traffic(), "traffic_unit": "HBM bytes per launch (rocprofv3 "
@@ -642,7 +846,10 @@ def main():
                      "col_gemm_us_min": round(hl["col_min"] * 1e3, 3),
                      "note": "each call bracketed by its own HIP events, after the timed region"},
         "hbm_copy_gbs": round(copy_gbs(torch), 1),
+        "peaks": device_peaks(),
     }
+    if not args.no_rows:
+        result["rooflines_other"] = other_rooflines(torch, tp)
     if not args.no_rows:
         result["rows"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                           for k, v in rows(torch, tp, args.steps, args.warmup).items()}

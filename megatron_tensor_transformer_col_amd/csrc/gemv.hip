@@ -11,7 +11,9 @@
 //    spreads over all 256 CUs, two workgroups per CU).
 //  * Each ring stage holds a 64-row slab of the strip (8 KiB) and the
 //    matching 16 x 64 slice of x (2 KiB); both move HBM -> LDS with
-//    global_load_lds_dwordx4 (no VGPR staging), three DMA ops per wave per
+//    global_load_lds_dwordx4 (no VGPR staging; the weights, read once per
+//    call, with the nontemporal hint: 16.4 -> 15.5 us per column GEMV and
+//    partial-sum pair over 8 rotating shards), three DMA ops per wave per
 //    stage, through a 3-deep ring: two stages (20 KiB) in flight per
 //    workgroup, ~10 MB over the chip.  Measured on the 58.7 MB decode
 //    shards, deeper rings (up to 6 stages, 30 MB in flight) were ~1 us
@@ -200,7 +202,7 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
     if (s != tail) {
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        dma16s(woff[j], Wn + (int64_t)(kr + (wave + 4 * j) * 8) * ldw, base + (wave + 4 * j) * 1024);
+        dma16s_nt(woff[j], Wn + (int64_t)(kr + (wave + 4 * j) * 8) * ldw, base + (wave + 4 * j) * 1024);
       if (lane < 32) dma16s(xoff, X + kr, base + GV_WSLAB * 2 + wave * 512);
     } else {
       // rows past K are clamped to K-1 (valid memory, matched by zero x in
@@ -211,7 +213,7 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
         const int rb = min(kr + (wave + 4 * j) * 8, K - 1);
         const int r = min(kr + (wave + 4 * j) * 8 + (lane >> 3), K - 1) - rb;
         const uint32_t off = woff[j] - (uint32_t)((int64_t)(lane >> 3) * ldw * 2) + (uint32_t)((int64_t)r * ldw * 2);
-        dma16s(off, Wn + (int64_t)rb * ldw, base + (wave + 4 * j) * 1024);
+        dma16s_nt(off, Wn + (int64_t)rb * ldw, base + (wave + 4 * j) * 1024);
       }
       if (lane < 32) dma16s(xoff_row, X, base + GV_WSLAB * 2 + wave * 512);
     }

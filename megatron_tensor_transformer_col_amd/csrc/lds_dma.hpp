@@ -28,6 +28,12 @@ __device__ __forceinline__ void dma16s(uint32_t voff, const void *sbase, uint32_
   asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
 }
 
+// Same, nontemporal: for data read once (decode weights), which should not
+// displace cached lines.
+__device__ __forceinline__ void dma16s_nt(uint32_t voff, const void *sbase, uint32_t lds) {
+  asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(sbase), "{m0}"(lds) : "memory");
+}
+
 // LDS byte address of a __shared__ pointer (wave-uniform).
 __device__ __forceinline__ uint32_t lds_addr(const uint16_t *p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 const void *)p);
