@@ -116,7 +116,7 @@ __device__ __forceinline__ void epilogue4(const GemmParams &p, int row, int col,
 }
 
 // Launchers of the LDS-DMA kernels (bf16; gemm_lds: K a multiple of 32,
-// gemm_k64: K a multiple of 64, no dual products); each returns
+// gemm_k64: K a multiple of 64, dual products NN only); each returns
 // hipErrorNotSupported when the shape/layout is not covered so that the
 // caller falls back to the next kernel.
 hipError_t launch_gemm_lds(const GemmArgs &a, hipStream_t s);

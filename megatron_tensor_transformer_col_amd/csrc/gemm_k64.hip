@@ -18,6 +18,10 @@
 //    epilogue (activation, staging, stores) the other keeps the matrix cores
 //    busy, which hides the erf-GELU of the column-parallel product.  256 x 256
 //    tiles (one workgroup per CU) serve products with whole rounds of them.
+//  * Dual products (SwiGLU: X.Wg and X.Wu) stage both weight slabs side by
+//    side and keep both accumulators of an output element in one wave, so
+//    the gate and up values meet in registers: 256 x 128 output tiles carry
+//    the same per-slab traffic and MFMA work as a 256 x 256 single product.
 //  * The compiler's register allocation is steered with the minimal-register
 //    scheduling strategy (build flag); the default one shuffled accumulators
 //    between AGPRs and VGPRs inside the loop.
@@ -145,31 +149,41 @@ struct FragAddr {
 
 // BM x BN tile per workgroup of 4 waves (WGM x WGN), STAGES-deep ring of
 // 64-deep slabs, OCC workgroups per CU.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT>
+// DUAL (NN only): two products X.B and X.B2 of the same output tile, B's
+// and B2's slabs side by side in the stage (BN = twice the output width);
+// each wave holds both accumulators of its output columns, so the SwiGLU
+// epilogues pair them in registers.
+template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT, bool DUAL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
 gemm_k64_kernel(GemmParams pin) {
   GemmParams p = pin;
   static_assert(WGM * WGN == NW, "4 waves");
-  constexpr int WTM = BM / WGM, WTN = BN / WGN;
-  constexpr int TM = WTM / 16, TN = WTN / 16;
+  static_assert(!DUAL || (LAYOUT == LAY_NN && !KCAT), "dual products are NN");
+  constexpr int BNO = DUAL ? BN / 2 : BN;  // output tile width
+  constexpr int WTM = BM / WGM, WTNO = BNO / WGN;
+  constexpr int TM = WTM / 16, TNO = WTNO / 16, TN = DUAL ? 2 * TNO : TNO;
   constexpr bool AK = LAYOUT != LAY_TN;  // A stored k-contiguous
   constexpr bool BK = LAYOUT == LAY_NT;  // B stored k-contiguous
   constexpr int A_EL = BM * LBK, B_EL = BN * LBK;
   constexpr int STAGE = A_EL + B_EL;  // elements
+  constexpr int B2_OFF = BNO * LBK * 2;  // byte offset of B2's slab after B's (dual)
   using ADma = typename std::conditional<AK, KDma<BM, false>, NDma<BM>>::type;
-  using BDma = typename std::conditional<BK, KDma<BN, KCAT>, NDma<BN>>::type;
-  constexpr int LOADS = ADma::PER_WAVE + BDma::PER_WAVE;  // DMA ops per wave per slab
+  using BDma = typename std::conditional<BK, KDma<BNO, KCAT>, NDma<BNO>>::type;
+  constexpr int LOADS = ADma::PER_WAVE + (DUAL ? 2 : 1) * BDma::PER_WAVE;  // DMA ops per wave per slab
   static_assert(STAGES >= 2 && LOADS * STAGES < 64, "pipeline depth");
 
   // epilogue staging: the finished tile goes through LDS (the ring is idle
   // by then) and leaves as 16-byte chunks of consecutive rows
   constexpr int LDS_CAP = 160 * 1024 / OCC;
   constexpr int OES = EPI == EPI_STORE_F32 ? 4 : 2;  // output element bytes
-  constexpr int SROW = BN * OES + 16;               // staged row bytes (16-byte pad)
-  constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32) && BM * SROW <= LDS_CAP;
-  constexpr int SR3 = BN * 2 + 16;
-  constexpr bool STAGED3 = EPI == EPI_GELU_BWD && 2 * BM * SR3 <= LDS_CAP;
-  static_assert(EPI != EPI_GELU_BWD || STAGED3, "GELU backward needs its staged epilogue");
+  constexpr int SROW = BNO * OES + 16;              // staged row bytes (16-byte pad)
+  constexpr bool STAGED = (EPI == EPI_STORE || EPI == EPI_GELU || EPI == EPI_STORE_F32 || EPI == EPI_SWIGLU) &&
+                          BM * SROW <= LDS_CAP;
+  constexpr int SR3 = BNO * 2 + 16;
+  constexpr bool BWD = EPI == EPI_GELU_BWD || EPI == EPI_SWIGLU_BWD;
+  constexpr bool STAGED3 = BWD && 2 * BM * SR3 <= LDS_CAP;
+  static_assert(!BWD || STAGED3, "the backward epilogues are staged");
+  static_assert(DUAL == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD), "SwiGLU epilogues need both products");
   constexpr int RING_B = STAGES * STAGE * 2;
   constexpr int STG_B = STAGED ? BM * SROW : (STAGED3 ? 2 * BM * SR3 : 0);
   static_assert(RING_B <= LDS_CAP && STG_B <= LDS_CAP, "LDS budget");
@@ -182,7 +196,7 @@ gemm_k64_kernel(GemmParams pin) {
   const int nk = p.K / LBK;
   int tm, tn;
   tile_of_block(p.tiles_m, p.tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = tn * BNO;
 
   const uint16_t *Ag = static_cast<const uint16_t *>(p.A);
   const uint16_t *Bg = static_cast<const uint16_t *>(p.B);
@@ -197,16 +211,20 @@ gemm_k64_kernel(GemmParams pin) {
   // m/n-type ones LBK rows
   const uint16_t *Ab = AK ? Ag + (int64_t)m0 * p.lda : Ag + m0;
   const uint16_t *Bb = BK ? Bg + (int64_t)n0 * p.ldb : Bg + n0;
-  const uint16_t *B2b = KCAT ? static_cast<const uint16_t *>(p.B2) + (int64_t)n0 * p.ldb2 : nullptr;
+  const uint16_t *B2b = KCAT   ? static_cast<const uint16_t *>(p.B2) + (int64_t)n0 * p.ldb2
+                        : DUAL ? static_cast<const uint16_t *>(p.B2) + n0
+                               : nullptr;
   const int64_t astep = AK ? LBK : (int64_t)LBK * p.lda;
   const int64_t bstep = BK ? LBK : (int64_t)LBK * p.ldb;
+  const int64_t b2step = (int64_t)LBK * p.ldb2;  // dual
 
   ADma da;
-  BDma db;
+  BDma db, db2;
   if constexpr (AK) da.init(p.lda, 0, m0, M, wave, lane);
   else da.init(p.lda, m0, M, wave, lane);
   if constexpr (BK) db.init(p.ldb, p.ldb2, n0, N, wave, lane);
   else db.init(p.ldb, n0, N, wave, lane);
+  if constexpr (DUAL) db2.init(p.ldb2, n0, N, wave, lane);
 
   const uint32_t sbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 const void *)smem);
   auto issue = [&](int kt, int stage) {
@@ -219,6 +237,7 @@ gemm_k64_kernel(GemmParams pin) {
       db.issue(second ? B2b + (k0 - p.K1) : Bb + k0, second, base + A_EL * 2, wave);
     } else {
       db.issue(Bb + kt * bstep, base + A_EL * 2, wave);
+      if constexpr (DUAL) db2.issue(B2b + kt * b2step, base + A_EL * 2 + B2_OFF, wave);
     }
   };
 
@@ -229,9 +248,9 @@ gemm_k64_kernel(GemmParams pin) {
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 
   FragAddr<AK, BM, WTM> fa;
-  FragAddr<BK, BN, WTN> fb;
+  FragAddr<BK, BNO, WTNO> fb;
   fa.init(0, wm * WTM, lane);
-  fb.init(A_EL * 2, wn * WTN, lane);
+  fb.init(A_EL * 2, wn * WTNO, lane);
   struct Frags {
     uint4 a[TM];
     uint4 b[TN];
@@ -241,7 +260,11 @@ gemm_k64_kernel(GemmParams pin) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) F.a[i] = fa.read(st, kc, i);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) F.b[j] = fb.read(st, kc, j);
+    for (int j = 0; j < TNO; ++j) F.b[j] = fb.read(st, kc, j);
+    if constexpr (DUAL) {
+#pragma unroll
+      for (int j = 0; j < TNO; ++j) F.b[TNO + j] = fb.read(st + B2_OFF, kc, j);
+    }
   };
   constexpr int N_DS = TM * (AK ? 1 : 2) + TN * (BK ? 1 : 2);
   constexpr int N_MFMA = TM * TN;
@@ -309,11 +332,11 @@ gemm_k64_kernel(GemmParams pin) {
   const int g = lane >> 4, l16 = lane & 15;
   if constexpr (STAGED) {
     using OutT = typename std::conditional<EPI == EPI_STORE_F32, float, uint16_t>::type;
-    constexpr int CPR = BN * OES / 16;  // 16-byte chunks per tile row
-    float bv[TN][4];
+    constexpr int CPR = BNO * OES / 16;  // 16-byte chunks per tile row
+    float bv[TNO][4];
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 16 + g * 4;
+    for (int j = 0; j < TNO; ++j) {
+      const int col = n0 + wn * WTNO + j * 16 + g * 4;
 #pragma unroll
       for (int r = 0; r < 4; ++r) bv[j][r] = 0.f;
       if (p.bias != nullptr && col < N) {
@@ -325,14 +348,15 @@ gemm_k64_kernel(GemmParams pin) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
+      for (int j = 0; j < TNO; ++j) {
         float v[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           v[r] = acc[i][j][r] + bv[j][r];
           if constexpr (EPI == EPI_GELU) v[r] = gelu_f(v[r]);
+          if constexpr (EPI == EPI_SWIGLU) v[r] = silu_f(v[r]) * acc[i][DUAL ? TNO + j : j][r];
         }
-        char *dst = smem + (wm * WTM + i * 16 + l16) * SROW + (wn * WTN + j * 16 + g * 4) * OES;
+        char *dst = smem + (wm * WTM + i * 16 + l16) * SROW + (wn * WTNO + j * 16 + g * 4) * OES;
         store4(reinterpret_cast<OutT *>(dst), v);
       }
     }
@@ -346,17 +370,19 @@ gemm_k64_kernel(GemmParams pin) {
     return;
   }
   if constexpr (STAGED3) {
-    // GELU backward: dH comes into LDS by coalesced 16-byte loads, then dZ
-    // and H are computed from the accumulators and dH one tile at a time,
-    // written to LDS and stored as whole row chunks (reading dH element by
-    // element between stores would wait on every store before it)
-    constexpr int CPR = BN * 2 / 16;
+    // activation backward: dH comes into LDS by coalesced 16-byte loads,
+    // then each output (GELU: dZ, H; SwiGLU: dZg, H, dZu) is computed from
+    // the accumulators and dH one tile at a time, written to LDS and stored
+    // as whole row chunks (reading dH element by element between stores
+    // would wait on every store before it)
+    constexpr int CPR = BNO * 2 / 16;
+    constexpr int NOUT = EPI == EPI_SWIGLU_BWD ? 3 : 2;
     char *dhs = smem;
     char *out = smem + BM * SR3;
     if (p.bias != nullptr) {
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wn * WTN + j * 16 + g * 4;
+      for (int j = 0; j < TNO; ++j) {
+        const int col = n0 + wn * WTNO + j * 16 + g * 4;
         float bv[4] = {0.f, 0.f, 0.f, 0.f};
         if (col < N) load4(static_cast<const uint16_t *>(p.bias) + col, bv);
 #pragma unroll
@@ -376,25 +402,34 @@ gemm_k64_kernel(GemmParams pin) {
     }
     __syncthreads();
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
+    for (int which = 0; which < NOUT; ++which) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int off = (wm * WTM + i * 16 + l16) * SR3 + (wn * WTN + j * 16 + g * 4) * 2;
+        for (int j = 0; j < TNO; ++j) {
+          const int off = (wm * WTM + i * 16 + l16) * SR3 + (wn * WTNO + j * 16 + g * 4) * 2;
           float dh[4], o[4];
           load4(reinterpret_cast<const uint16_t *>(dhs + off), dh);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float z = acc[i][j][r];
-            o[r] = which == 0 ? dh[r] * gelu_grad_f(z) : gelu_f(z);
+            if constexpr (EPI == EPI_GELU_BWD) {
+              o[r] = which == 0 ? dh[r] * gelu_grad_f(z) : gelu_f(z);
+            } else {
+              // z = gate pre-activation, u = up projection
+              const float u = acc[i][DUAL ? TNO + j : j][r];
+              const float sg = sigmoid_f(z);
+              const float sl = z * sg;
+              o[r] = which == 0 ? dh[r] * u * (sg * (1.0f + z * (1.0f - sg))) : (which == 1 ? sl * u : dh[r] * sl);
+            }
           }
           store4(reinterpret_cast<uint16_t *>(out + off), o);
         }
       }
       __syncthreads();
-      void *C = which == 0 ? p.C : p.C2;  // dZ -> C, H -> C2
-      const int64_t ldc = which == 0 ? p.ldc : p.ldc2;
+      // dZ (dZg) -> C, H -> C2, dZu -> C3
+      void *C = which == 0 ? p.C : (which == 1 ? p.C2 : p.C3);
+      const int64_t ldc = which == 0 ? p.ldc : (which == 1 ? p.ldc2 : p.ldc3);
       for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
         const int rl = c / CPR, cc = c % CPR;
         const int row = m0 + rl, col = n0 + cc * 8;
@@ -410,19 +445,22 @@ gemm_k64_kernel(GemmParams pin) {
   for (int i = 0; i < TM; ++i) {
     const int row = m0 + wm * WTM + i * 16 + l16;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wn * WTN + j * 16 + g * 4;
+    for (int j = 0; j < TNO; ++j) {
+      const int col = n0 + wn * WTNO + j * 16 + g * 4;
       if (row >= M || col >= N) continue;
       float v[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
-      const float u[4] = {0.f, 0.f, 0.f, 0.f};
+      const int ju = DUAL ? TNO + j : j;
+      const float u[4] = {acc[i][ju][0], acc[i][ju][1], acc[i][ju][2], acc[i][ju][3]};
       epilogue4<uint16_t, EPI>(p, row, col, v, u);
     }
   }
 }
 
 // ---------------------------------------------------------------- host side
-template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT>
+template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT,
+          bool DUAL = false>
 static hipError_t run(const GemmArgs &a, hipStream_t s) {
+  constexpr int BNO = DUAL ? BN / 2 : BN;
   GemmParams p;
   p.A = a.A; p.lda = a.lda;
   p.B = a.B; p.ldb = a.ldb;
@@ -434,9 +472,9 @@ static hipError_t run(const GemmArgs &a, hipStream_t s) {
   p.C3 = a.C3; p.ldc3 = a.ldc3;
   p.M = (int)a.M; p.N = (int)a.N; p.K = (int)a.K; p.K1 = (int)a.K1;
   p.tiles_m = (int)((a.M + BM - 1) / BM);
-  p.tiles_n = (int)((a.N + BN - 1) / BN);
+  p.tiles_n = (int)((a.N + BNO - 1) / BNO);
   p.zstride = a.zstride;
-  hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT>),
+  hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT, DUAL>),
                      dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)a.splits), dim3(NW * 64), 0, s, p);
   return hipGetLastError();
 }
@@ -452,35 +490,97 @@ static int64_t cus() {
   return n;
 }
 
-// 256 x 256 tiles (one workgroup per CU) when they come in whole rounds over
-// the CUs; otherwise 128 x 128 tiles, two workgroups per CU.
+// 256 x 256 tiles (one workgroup per CU) or 128 x 128 tiles (two per CU),
+// whichever takes fewer rounds over the CUs: a CU runs a pair of 128 x 128
+// tiles (half a 256 x 256 tile's work) in about 0.62 of a 256 x 256 tile's
+// time (measured on 4096 x 3584 x 8192 and 8192 x 3584 x 4096 products), and
+// the 128 x 128 tiles spread evenly while the last round of 256 x 256 ones
+// may leave CUs idle.  The activation epilogues stay on 128 x 128 tiles,
+// where the other workgroup of the CU hides them.
 template <int LAYOUT, int EPI, bool KCAT>
 static hipError_t pick(const GemmArgs &a, hipStream_t s) {
   const int64_t n = cus();
   const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
+  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits;
   constexpr bool BIG_OK = EPI == EPI_STORE || EPI == EPI_STORE_F32;
   if constexpr (BIG_OK) {
-    if (t256 >= n && t256 % n == 0) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
+    const double big_rounds = (double)((t256 + n - 1) / n);
+    const double pair_rounds = 0.62 * (double)t128 / (double)(2 * n);
+    if (big_rounds < pair_rounds) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
   }
   return run<128, 128, 2, 2, 2, 2, LAYOUT, EPI, KCAT>(a, s);
+}
+
+// The output columns [c0, c0 + nc) of a dual (bf16, NN) product: the
+// weights, outputs, epilogue input and bias shifted by c0 columns.
+static GemmArgs dual_cols(const GemmArgs &a, int64_t c0, int64_t nc) {
+  GemmArgs b = a;
+  b.N = nc;
+  auto sh = [c0](const void *q) { return q == nullptr ? nullptr : static_cast<const uint16_t *>(q) + c0; };
+  auto shm = [c0](void *q) { return q == nullptr ? nullptr : static_cast<uint16_t *>(q) + c0; };
+  b.B = sh(a.B);
+  b.B2 = sh(a.B2);
+  b.bias = sh(a.bias);
+  b.D = sh(a.D);
+  b.C = shm(a.C);
+  b.C2 = shm(a.C2);
+  b.C3 = shm(a.C3);
+  return b;
+}
+
+// Dual (SwiGLU) products: 256 x 128 output tiles (a 256 x 256 stage with
+// both weight slabs, one workgroup per CU) and 128 x 128 ones (one per CU
+// too, half the work per tile).  The leading c column-tiles take the large
+// tiles and the rest the small ones, with c chosen to minimise the number
+// of rounds over the CUs, a large-tile round costing about 1.6 small-tile
+// rounds (measured on the SwiGLU shard: 8192 x 3584 x 4096 in 397 us with
+// large tiles only, 428 us with small ones, 375 us with 24 of the 28
+// column-tiles large, i.e. three whole rounds of them and one of small ones).
+template <int EPI>
+static hipError_t pick_dual(const GemmArgs &a, hipStream_t s) {
+  const int64_t n = cus();
+  const int64_t tmb = (a.M + 255) / 256, tms = (a.M + 127) / 128, tn = (a.N + 127) / 128;
+  auto rounds = [n](int64_t tiles) { return (tiles + n - 1) / n; };
+  int64_t best_c = tn;
+  double best = 1e30;
+  for (int64_t c = tn; c >= 0; --c) {
+    const double cost = 1.6 * (double)rounds(tmb * c) + (double)rounds(tms * (tn - c)) +
+                        (c > 0 && c < tn ? 0.25 : 0.0);  // a second launch
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_c = c;
+    }
+  }
+  const int64_t c0 = std::min(best_c * 128, a.N);
+  if (c0 > 0) {
+    const hipError_t e = run<256, 256, 2, 2, 2, 1, LAY_NN, EPI, false, true>(c0 < a.N ? dual_cols(a, 0, c0) : a, s);
+    if (e != hipSuccess || c0 == a.N) return e;
+  }
+  return run<128, 256, 2, 2, 2, 1, LAY_NN, EPI, false, true>(c0 > 0 ? dual_cols(a, c0, a.N - c0) : a, s);
 }
 
 }  // namespace k64
 
 hipError_t launch_gemm_k64(const GemmArgs &a, hipStream_t s) {
   using namespace k64;
-  if (a.dtype != DT_BF16 || a.dual || a.K <= 0 || a.K % LBK != 0) return hipErrorNotSupported;
+  if (a.dtype != DT_BF16 || a.K <= 0 || a.K % LBK != 0) return hipErrorNotSupported;
+  if (a.dual && (a.layout != LAY_NN || a.kcat || (a.epi != EPI_SWIGLU && a.epi != EPI_SWIGLU_BWD)))
+    return hipErrorNotSupported;
   if (a.kcat && (a.K1 % LBK != 0 || a.layout != LAY_NT)) return hipErrorNotSupported;
   if (a.M < 8 || a.N < 8) return hipErrorNotSupported;
   // the DMA offsets are 32-bit (up to 256 rows of a k-contiguous operand or
   // 64 rows of an m/n-contiguous one, relative to the slab base)
-  const int64_t ld_max = std::max(a.lda, std::max(a.ldb, a.kcat ? a.ldb2 : (int64_t)0));
+  const int64_t ld_max = std::max(a.lda, std::max(a.ldb, a.kcat || a.dual ? a.ldb2 : (int64_t)0));
   if (ld_max * 2 * 256 >= ((int64_t)1 << 32)) return hipErrorNotSupported;
   // small products stay on the other kernels (more, smaller tiles)
   if (((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits < 128) return hipErrorNotSupported;
   if (a.splits > 1 && (a.layout != LAY_TN || a.epi != EPI_STORE_F32)) return hipErrorInvalidValue;
   switch (a.layout) {
     case LAY_NN:
+      if (a.dual) {
+        if (a.epi == EPI_SWIGLU) return pick_dual<EPI_SWIGLU>(a, s);
+        return pick_dual<EPI_SWIGLU_BWD>(a, s);
+      }
       switch (a.epi) {
         case EPI_STORE: return pick<LAY_NN, EPI_STORE, false>(a, s);
         case EPI_STORE_F32: return pick<LAY_NN, EPI_STORE_F32, false>(a, s);

@@ -150,7 +150,11 @@ def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     assert_close(host(dX), ref["dX"], "bf16", "dX")
 
 
-@pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (520, 256, 2048, 1), (1024, 1024, 2048, 2)])
+# the last three take the 64-deep dual GEMM with ragged token and ffn edges:
+# 128 x 128 output tiles only, 256 x 128 ones only, and 15 column-tiles of
+# 256 x 128 followed by 128 x 128 ones
+@pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (520, 256, 2048, 1), (1024, 1024, 2048, 2),
+                                        (1100, 256, 2048, 1), (2100, 512, 2064, 1), (4200, 256, 2056, 1)])
 def test_mlp_swiglu_bf16_medium(T_, h, ffn, n):
     note(f"bf16 SwiGLU fwd+bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_swiglu_inputs(T_, h, ffn, "bf16", seed=3, with_dy=True)
