@@ -344,9 +344,12 @@ int tp_vocab_ce_total(int n, const float *const *shard_losses, float *total, voi
  *   Outputs (float32, dense): dW1 [K x Ni], dWup [K x Ni] (SwiGLU else NULL),
  *   dW2 [Ni x K], db1 [Ni] (optional; GELU only), dXi [M x K] ldd x.
  *   ws: tp_mlp_shard_backward_workspace() bytes; holds dH_i, H_i and dZ_i
- *   ([M x Ni] each, dtype; dZg and dZu for SwiGLU) and, without SwiGLU,
- *   up to 64 fp32 rows [64 x Ni] of partial column sums for db1 (summed in
- *   a fixed order, so db1 is deterministic).
+ *   ([M x Ni] each, dtype; dZg and dZu for SwiGLU) and, without SwiGLU, a
+ *   second dH-sized region and up to 64 fp32 rows [64 x Ni] of partial
+ *   column sums for db1.  After the recompute the dH region (GELU: with the
+ *   region after it) holds fp32 K-range partials of the weight gradients.
+ *   Every partial is added in a fixed order, so all outputs are
+ *   deterministic.
  */
 int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni,
                           const void *X, int64_t ldx,

@@ -108,20 +108,23 @@ bool use_gemv(int dtype, int64_t M) {
   return dtype == TP_BF16 && M >= 1 && M <= g_gemv_max_m.load(std::memory_order_relaxed);
 }
 
-// Backward workspace layout: dH [M x Ni], H [M x Ni], dZ [M x Ni] (GELU) or
-// [M x 2Ni] = [dZg | dZu] (SwiGLU); each region 256-byte aligned.
+// Backward workspace layout: dH [M x Ni], (GELU: as much again,) H [M x Ni],
+// dZ [M x Ni] (GELU) or [M x 2Ni] = [dZg | dZu] (SwiGLU); each region
+// 256-byte aligned.  Once the recompute has consumed dH, [dH, H) holds the
+// fp32 K-range partials of the weight-gradient products.
 struct BwdWs {
   size_t dH, H, dZ, cs, total;
 };
 // dH_i, H_i, dZ_i (SwiGLU: [dZg | dZu]); GELU / no activation also the
-// fp32 column-sum partials of db1
+// fp32 column-sum partials of db1 and a second dH-sized region, so that the
+// two weight gradients' partials fit together
 BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
   const size_t e = esize(dtype);
   const size_t one = round256((size_t)M * (size_t)Ni * e);
   BwdWs w;
   w.dH = 0;
-  w.H = one;
-  w.dZ = 2 * one;
+  w.H = act == TP_ACT_SWIGLU ? one : 2 * one;
+  w.dZ = w.H + one;
   w.cs = w.dZ + (act == TP_ACT_SWIGLU ? round256((size_t)M * 2 * (size_t)Ni * e) : one);
   w.total = w.cs + (act == TP_ACT_SWIGLU ? 0 : round256(colsum_workspace(Ni)));
   return w;
@@ -737,31 +740,31 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
   }
 
   // dW2 = H^T dY (row-parallel weight gradient)
-  {
-    GemmArgs w;
-    w.dtype = dtype; w.layout = LAY_TN; w.epi = EPI_STORE_F32;
-    w.M = Ni; w.N = K; w.K = M;
-    w.A = H; w.lda = Ni;
-    w.B = dY; w.ldb = lddy;
-    w.C = dW2; w.ldc = K;
-    w.part = dHpart; w.part_bytes = dHpart_bytes;
-    TRY(hip_status(launch_gemm(w, s), "dW2 GEMM"));
-  }
+  GemmArgs w2;
+  w2.dtype = dtype; w2.layout = LAY_TN; w2.epi = EPI_STORE_F32;
+  w2.M = Ni; w2.N = K; w2.K = M;
+  w2.A = H; w2.lda = Ni;
+  w2.B = dY; w2.ldb = lddy;
+  w2.C = dW2; w2.ldc = K;
+  w2.part = dHpart; w2.part_bytes = dHpart_bytes;
   // dW1 = X^T dZ (column-parallel weight gradient; dWup = X^T dZu)
-  {
-    GemmArgs w;
-    w.dtype = dtype; w.layout = LAY_TN; w.epi = EPI_STORE_F32;
-    w.M = K; w.N = Ni; w.K = M;
-    w.A = X; w.lda = ldx;
-    w.B = dZ; w.ldb = ldz;
-    w.C = dW1; w.ldc = Ni;
-    w.part = dHpart; w.part_bytes = dHpart_bytes;
-    TRY(hip_status(launch_gemm(w, s), "dW1 GEMM"));
-    if (swiglu) {
-      w.B = dZu;
-      w.C = dWup;
-      TRY(hip_status(launch_gemm(w, s), "dWup GEMM"));
-    }
+  GemmArgs w1;
+  w1.dtype = dtype; w1.layout = LAY_TN; w1.epi = EPI_STORE_F32;
+  w1.M = K; w1.N = Ni; w1.K = M;
+  w1.A = X; w1.lda = ldx;
+  w1.B = dZ; w1.ldb = ldz;
+  w1.C = dW1; w1.ldc = Ni;
+  w1.part = dHpart; w1.part_bytes = dHpart_bytes;
+  if (swiglu) {
+    // dWg and dWu have the same shape: one launch when they split
+    GemmArgs wu = w1;
+    wu.B = dZu;
+    wu.C = dWup;
+    TRY(hip_status(launch_gemm(w2, s), "dW2 GEMM"));
+    TRY(hip_status(launch_gemm_tn_pair(w1, wu, s), "dW1 / dWup GEMMs"));
+  } else {
+    // one launch for both when they have the same shape (K == Ni) and split
+    TRY(hip_status(launch_gemm_tn_pair(w2, w1, s), "dW2 / dW1 GEMMs"));
   }
   if (db1 != nullptr) {
     float *cs = M > 0 ? reinterpret_cast<float *>(base + L.cs) : nullptr;  // M == 0: db1 = 0

@@ -356,6 +356,47 @@ static hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
   return launch_gemm_lds(a, s);
 }
 
+// Both weight gradients of a backward in one launch: K-range splits of the
+// two products share the grid (rows [0, S) the first, [S, 2S) the second),
+// so that narrow outputs fill two workgroups per CU, then one launch adds
+// each product's partials in split order.
+hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream_t s) {
+  auto separate = [&]() -> hipError_t {
+    const hipError_t e = launch_gemm(a0, s);
+    if (e != hipSuccess) return e;
+    return launch_gemm(a1, s);
+  };
+  if (a0.M <= 0 || a0.N <= 0 || a0.dtype != DT_BF16 || a1.dtype != DT_BF16 || a0.layout != LAY_TN ||
+      a1.layout != LAY_TN || a0.epi != EPI_STORE_F32 || a1.epi != EPI_STORE_F32 || a0.bias != nullptr ||
+      a1.bias != nullptr || a0.M != a1.M || a0.N != a1.N || a0.K != a1.K || a0.part == nullptr || a0.N % 4)
+    return separate();
+  const int64_t tiles = ((a0.M + 127) / 128) * ((a0.N + 127) / 128);
+  const size_t one = (size_t)a0.M * (size_t)a0.N * sizeof(float);
+  // two workgroups per CU over 256 CUs, splits at least 512 deep, the
+  // partials of both products inside the scratch
+  int S = 1;
+  while (S < 8 && 2 * tiles * 2 * S <= 512 && (size_t)(2 * 2 * S) * one <= a0.part_bytes &&
+         a0.K % (64 * 2 * S) == 0 && a0.K / (2 * S) >= 512)
+    S *= 2;
+  if (S == 1) return separate();
+  GemmArgs b = a0;
+  b.splits = S;
+  b.groups = 2;
+  b.K = a0.K / S;
+  b.C = a0.part;
+  b.ldc = a0.N;
+  b.zstride = a0.M * a0.N;
+  b.A2 = a1.A; b.lda2 = a1.lda;
+  b.B2 = a1.B; b.ldb2 = a1.ldb;
+  const hipError_t e = launch_gemm_k64(b, s);
+  if (e == hipErrorNotSupported) return separate();
+  if (e != hipSuccess) return e;
+  const float *parts[16];
+  for (int z = 0; z < 2 * S; ++z) parts[z] = a0.part + (int64_t)z * b.zstride;
+  return launch_shard_sum_pair(a0.M, a0.N, S, parts, a0.N, static_cast<float *>(a0.C), a0.ldc,
+                               static_cast<float *>(a1.C), a1.ldc, s);
+}
+
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.dtype == DT_BF16) {

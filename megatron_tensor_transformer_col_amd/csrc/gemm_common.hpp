@@ -20,6 +20,9 @@ struct GemmParams {
   int M, N, K, K1;  // K: depth of one K-range split
   int tiles_m, tiles_n;
   int64_t zstride;   // elements between split outputs (TN split-K only)
+  // grouped TN split-K: grid rows [zsplit, 2 zsplit) compute A2^T B2
+  const void *A2; int64_t lda2;
+  int zsplit;
 };
 
 template <typename T>

@@ -201,11 +201,20 @@ gemm_k64_kernel(GemmParams pin) {
   const uint16_t *Ag = static_cast<const uint16_t *>(p.A);
   const uint16_t *Bg = static_cast<const uint16_t *>(p.B);
   if constexpr (LAYOUT == LAY_TN) {
-    // split-K: grid row z takes K rows [z K, (z+1) K) and writes its own partial
-    const int z = blockIdx.y;
+    // split-K: grid row y = g zsplit + z takes K rows [z K, (z+1) K) of
+    // product g (g = 1: A2^T B2) and writes partial y
+    const int y = blockIdx.y;
+    const int g = y >= p.zsplit ? 1 : 0;
+    const int z = y - g * p.zsplit;
+    if (g) {
+      Ag = static_cast<const uint16_t *>(p.A2);
+      p.lda = p.lda2;
+      Bg = static_cast<const uint16_t *>(p.B2);
+      p.ldb = p.ldb2;
+    }
     Ag += (int64_t)z * p.K * p.lda;
     Bg += (int64_t)z * p.K * p.ldb;
-    p.C = static_cast<float *>(p.C) + (int64_t)z * p.zstride;
+    p.C = static_cast<float *>(p.C) + (int64_t)y * p.zstride;
   }
   // wave-uniform slab bases: k-type operands advance LBK elements per slab,
   // m/n-type ones LBK rows
@@ -474,8 +483,11 @@ static hipError_t run(const GemmArgs &a, hipStream_t s) {
   p.tiles_m = (int)((a.M + BM - 1) / BM);
   p.tiles_n = (int)((a.N + BNO - 1) / BNO);
   p.zstride = a.zstride;
+  p.A2 = a.A2; p.lda2 = a.lda2;
+  p.zsplit = a.splits;
   hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT, DUAL>),
-                     dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)a.splits), dim3(NW * 64), 0, s, p);
+                     dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)(a.splits * a.groups)), dim3(NW * 64), 0, s,
+                     p);
   return hipGetLastError();
 }
 
@@ -500,8 +512,8 @@ static int64_t cus() {
 template <int LAYOUT, int EPI, bool KCAT>
 static hipError_t pick(const GemmArgs &a, hipStream_t s) {
   const int64_t n = cus();
-  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits;
-  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits;
+  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits * a.groups;
+  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits * a.groups;
   constexpr bool BIG_OK = EPI == EPI_STORE || EPI == EPI_STORE_F32;
   if constexpr (BIG_OK) {
     const double big_rounds = (double)((t256 + n - 1) / n);
@@ -570,11 +582,14 @@ hipError_t launch_gemm_k64(const GemmArgs &a, hipStream_t s) {
   if (a.M < 8 || a.N < 8) return hipErrorNotSupported;
   // the DMA offsets are 32-bit (up to 256 rows of a k-contiguous operand or
   // 64 rows of an m/n-contiguous one, relative to the slab base)
-  const int64_t ld_max = std::max(a.lda, std::max(a.ldb, a.kcat || a.dual ? a.ldb2 : (int64_t)0));
+  if (a.groups != 1 && (a.groups != 2 || a.layout != LAY_TN || a.A2 == nullptr || a.B2 == nullptr))
+    return hipErrorInvalidValue;
+  const int64_t ld_max = std::max(std::max(a.lda, a.groups > 1 ? a.lda2 : (int64_t)0),
+                                  std::max(a.ldb, a.kcat || a.dual || a.groups > 1 ? a.ldb2 : (int64_t)0));
   if (ld_max * 2 * 256 >= ((int64_t)1 << 32)) return hipErrorNotSupported;
   // small products stay on the other kernels (more, smaller tiles)
-  if (((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits < 128) return hipErrorNotSupported;
-  if (a.splits > 1 && (a.layout != LAY_TN || a.epi != EPI_STORE_F32)) return hipErrorInvalidValue;
+  if (((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits * a.groups < 128) return hipErrorNotSupported;
+  if ((a.splits > 1 || a.groups > 1) && (a.layout != LAY_TN || a.epi != EPI_STORE_F32)) return hipErrorInvalidValue;
   switch (a.layout) {
     case LAY_NN:
       if (a.dual) {

@@ -47,9 +47,17 @@ struct GemmArgs {
   // set by launch_gemm for the LDS kernel: K-range splits (grid y) and the
   // element stride between their outputs
   int splits = 1; int64_t zstride = 0;
+  // grouped TN split-K (launch_gemm_tn_pair): a second product of the same
+  // shape, A2 . B2 (B2 / ldb2 above), whose partials follow the first's
+  const void *A2 = nullptr; int64_t lda2 = 0;
+  int groups = 1;
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// Two bf16 TN fp32 products of the same shape (a0.C = A0^T B0, a1.C =
+// A1^T B1): one K-split launch for both when a0.part holds their partials,
+// else two launch_gemm calls.
+hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream_t s);
 
 // Decode GEMV (M <= 16): y = act(x W + bias) with split-K partials in ws.
 struct GemvArgs {
@@ -76,6 +84,10 @@ size_t gemv_noalloc_max_bytes();
 // Y = sum_i P_i (+ bias), float32 partials, float32 or bf16 output.
 hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *parts,
                             int64_t ldp, const float *bias, void *Y, int64_t ldy, hipStream_t s);
+// Two such sums in one launch (fp32 outputs, no bias): Y0 = sum_i P_i,
+// Y1 = sum_i P_{n+i} for i < n.
+hipError_t launch_shard_sum_pair(int64_t M, int64_t N, int n, const float *const *parts, int64_t ldp,
+                                 float *Y0, int64_t ldy0, float *Y1, int64_t ldy1, hipStream_t s);
 
 // Head-local flash attention over a packed [Q|K|V] buffer (bf16, d = 128).
 // lse (optional, [b][heads_local][s] fp32): log2 of each query row's softmax

@@ -41,6 +41,41 @@ shard_sum_kernel(PartialPtrs pp, int n, int64_t M, int64_t N4, int64_t ldp, cons
   }
 }
 
+// Two sums of n partials each (fp32 out): element v of the combined range
+// [0, 2 M N4) belongs to sum g = v / (M N4), whose terms are P_{g n + i}.
+__global__ void __launch_bounds__(256)
+shard_sum_pair_kernel(PartialPtrs pp, int n, int64_t M, int64_t N4, int64_t ldp, float *Y0, int64_t ldy0,
+                      float *Y1, int64_t ldy1) {
+  const int64_t one = M * N4;
+  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < 2 * one;
+       v += (int64_t)gridDim.x * blockDim.x) {
+    const int g = v >= one ? 1 : 0;
+    const int64_t w = v - g * one;
+    const int64_t row = w / N4, c = (w - row * N4) * 4;
+    const int64_t off = row * ldp + c;
+    const float *const *p = pp.p + g * n;
+    float4 acc = *reinterpret_cast<const float4 *>(p[0] + off);
+    for (int i = 1; i < n; ++i) {
+      const float4 t = *reinterpret_cast<const float4 *>(p[i] + off);
+      acc.x += t.x; acc.y += t.y; acc.z += t.z; acc.w += t.w;
+    }
+    *reinterpret_cast<float4 *>((g ? Y1 + row * ldy1 : Y0 + row * ldy0) + c) = acc;
+  }
+}
+
+hipError_t launch_shard_sum_pair(int64_t M, int64_t N, int n, const float *const *parts, int64_t ldp,
+                                 float *Y0, int64_t ldy0, float *Y1, int64_t ldy1, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (n < 1 || 2 * n > kMaxShards || N % 4) return hipErrorInvalidValue;
+  PartialPtrs pp;
+  for (int i = 0; i < kMaxShards; ++i) pp.p[i] = parts[i < 2 * n ? i : 0];
+  const int64_t N4 = N / 4;
+  const int64_t want = (2 * M * N4 + 255) / 256;
+  const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
+  hipLaunchKernelGGL(shard_sum_pair_kernel, dim3(grid), dim3(256), 0, s, pp, n, M, N4, ldp, Y0, ldy0, Y1, ldy1);
+  return hipGetLastError();
+}
+
 hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *parts,
                             int64_t ldp, const float *bias, void *Y, int64_t ldy, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;

@@ -68,11 +68,12 @@ def test_workspace_sizes():
     assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 8, 128) == T * 1024 * 2 + T * 8 * 4 + T * 24 * 128 * 2
     assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 128) == (
         T * 1024 * 2 + T * 8 * 4 + T * 12 * 128 * 2 + 4 * T * 2 * 2 * 128 * 4)
-    # backward: dH, H, dZ and 64 fp32 rows of db1 column-sum partials (GELU) /
+    # backward: dH, a dH-sized partial region, H, dZ and 64 fp32 rows of db1
+    # column-sum partials (GELU) /
     # dH, H, [dZg | dZu] (SwiGLU, no bias)
-    assert tp.tp_mlp_shard_backward_workspace(1, 1, 8192, 1024) == 3 * 8192 * 1024 * 2 + 64 * 1024 * 4
+    assert tp.tp_mlp_shard_backward_workspace(1, 1, 8192, 1024) == 4 * 8192 * 1024 * 2 + 64 * 1024 * 4
     assert tp.tp_mlp_shard_backward_workspace(1, 2, 8192, 3584) == 4 * 8192 * 3584 * 2
-    assert tp.tp_mlp_shard_backward_workspace(0, 1, 32, 256) == 3 * 32 * 256 * 4 + 64 * 256 * 4
+    assert tp.tp_mlp_shard_backward_workspace(0, 1, 32, 256) == 4 * 32 * 256 * 4 + 64 * 256 * 4
     # large-M linear calls need no workspace; the decode path needs split-K partials
     assert tp.tp_col_linear_gelu_workspace(1, 1, 8192, 1024, 1024) == 0
     assert tp.tp_col_linear_gelu_workspace(1, 1, 16, 8192, 3584) > 0

@@ -135,7 +135,12 @@ def test_mlp_gelu_bf16_medium(T_, h, ffn, n):
                                         # splits added in order from the dead dH scratch
                                         (4096, 512, 1024, 1),
                                         # ragged [264 x 520] weight gradients, 8 splits
-                                        (8192, 264, 520, 1)])
+                                        (8192, 264, 520, 1),
+                                        # dW1 and dW2 of one shape [512 x 512]: one launch,
+                                        # 4 K-range splits each, one launch adds both
+                                        (4096, 512, 512, 1),
+                                        # the GPT-2-medium shard's shapes (h 1024, ffn 1024)
+                                        (8192, 1024, 1024, 1)])
 def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     note(f"bf16 MLP GELU bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_mlp_inputs(T_, h, ffn, "bf16", seed=2, with_dy=True, with_bias=True)
@@ -246,21 +251,22 @@ def test_llama_swiglu_full_size_sampled():
     assert_close(host(dWd[ci]), gw["dWd"], "bf16", "dWd_0 rows")
 
 
-def test_mlp_backward_repeats_bitwise():
-    # split-K weight gradients (4 splits here) and db1 add their partials in a
-    # fixed order: repeated calls give identical bits, whatever the
-    # workspace held before
-    note("bf16 MLP GELU bwd repeatability 4096x512x1024")
+@pytest.mark.parametrize("h,ffn", [(512, 1024), (512, 512)])
+def test_mlp_backward_repeats_bitwise(h, ffn):
+    # split-K weight gradients (4 splits here; the [512 x 512] pair in one
+    # launch) and db1 add their partials in a fixed order: repeated calls give
+    # identical bits, whatever the workspace held before
+    note(f"bf16 MLP GELU bwd repeatability 4096x{h}x{ffn}")
     T = torch()
-    d = synth.make_mlp_inputs(4096, 512, 1024, "bf16", seed=5, with_dy=True, with_bias=True)
+    d = synth.make_mlp_inputs(4096, h, ffn, "bf16", seed=5, with_dy=True, with_bias=True)
     X, W1, W2, dY, b1 = dev(d["X"]), dev(d["W1"]), dev(d["W2"]), dev(d["dY"]), dev(d["b1"])[0]
-    nbytes = tp.tp_mlp_shard_backward_workspace(tp.TP_BF16, tp.TP_ACT_GELU_ERF, 4096, 1024)
+    nbytes = tp.tp_mlp_shard_backward_workspace(tp.TP_BF16, tp.TP_ACT_GELU_ERF, 4096, ffn)
     ws = T.empty((nbytes,), dtype=T.uint8, device="cuda:0")
     runs = []
     for it in range(3):
         ws.fill_(it * 85)
-        o = {"dW1": empty((512, 1024), "f32"), "dW2": empty((1024, 512), "f32"),
-             "dX": empty((4096, 512), "f32"), "db1": empty((1, 1024), "f32")}
+        o = {"dW1": empty((h, ffn), "f32"), "dW2": empty((ffn, h), "f32"),
+             "dX": empty((4096, h), "f32"), "db1": empty((1, ffn), "f32")}
         tp.tp_mlp_shard_backward(X, W1, W2, dY, o["dW1"], o["dW2"], o["dX"], act="gelu", b1=b1,
                                  db1=o["db1"][0], ws=ws)
         T.cuda.synchronize()
