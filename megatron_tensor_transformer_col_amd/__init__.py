@@ -35,7 +35,10 @@ TP_F32, TP_BF16 = 0, 1
 TP_ACT_NONE, TP_ACT_GELU_ERF, TP_ACT_SWIGLU = 0, 1, 2
 _ACTS = {"none": TP_ACT_NONE, "gelu": TP_ACT_GELU_ERF, "swiglu": TP_ACT_SWIGLU}
 
-library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpcol.so")
+# TPCOL_LIBRARY selects another build of the same library (the sanitizer
+# build of the host code, for the CPU ABI tests)
+library_path = os.environ.get("TPCOL_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                               "libtpcol.so")
 
 _i64, _sz, _vp, _int = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int
 _SIGS = {
