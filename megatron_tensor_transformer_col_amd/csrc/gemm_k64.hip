@@ -502,23 +502,66 @@ static int64_t cus() {
   return n;
 }
 
-// 256 x 256 tiles (one workgroup per CU) or 128 x 128 tiles (two per CU),
-// whichever takes fewer rounds over the CUs: a CU runs a pair of 128 x 128
-// tiles (half a 256 x 256 tile's work) in about 0.62 of a 256 x 256 tile's
-// time (measured on 4096 x 3584 x 8192 and 8192 x 3584 x 4096 products), and
-// the 128 x 128 tiles spread evenly while the last round of 256 x 256 ones
-// may leave CUs idle.  The activation epilogues stay on 128 x 128 tiles,
-// where the other workgroup of the CU hides them.
+// The output columns [c0, c0 + nc) of a single product: B (and the second
+// K source), C and the bias shifted by c0 columns (B's columns are its rows
+// when it is stored [N x K]).
+template <int LAYOUT, int EPI>
+static GemmArgs single_cols(const GemmArgs &a, int64_t c0, int64_t nc) {
+  constexpr size_t CE = EPI == EPI_STORE_F32 ? 4 : 2;  // output / bias element bytes
+  GemmArgs b = a;
+  b.N = nc;
+  b.B = static_cast<const uint16_t *>(a.B) + (LAYOUT == LAY_NT ? c0 * a.ldb : c0);
+  if (a.kcat) b.B2 = static_cast<const uint16_t *>(a.B2) + c0 * a.ldb2;  // NT: rows are columns
+  b.C = static_cast<char *>(a.C) + c0 * CE;
+  if (a.bias != nullptr) b.bias = static_cast<const char *>(a.bias) + c0 * CE;
+  return b;
+}
+
+// Launch rounds of a plan, in units of a round of 256 x 256 tiles: a CU runs
+// a pair of 128 x 128 tiles (half a 256 x 256 tile's work) in about 0.62 of
+// a 256 x 256 tile's time (measured on 4096 x 3584 x 8192 and
+// 8192 x 3584 x 4096 products); 128 x 128 tiles spread evenly over the two
+// slots of every CU (counted in half rounds), while the last round of
+// 256 x 256 tiles may leave CUs idle.  A second launch costs ~0.17.
+static double plan_cost(int64_t big_tiles, int64_t small_tiles, int64_t n) {
+  const double big = (double)((big_tiles + n - 1) / n);
+  const double small = 0.5 * (double)((small_tiles + n - 1) / n);  // pair rounds, half-round steps
+  return big + 0.62 * small + (big_tiles > 0 && small_tiles > 0 ? 0.17 : 0.0);
+}
+
+// 256 x 256 tiles (one workgroup per CU) for the leading c column-tiles and
+// 128 x 128 tiles (two per CU) for the rest, c chosen by plan_cost (8192 x
+// 3072 x 4096: 183 us with small tiles only, 197 us large only, 176 us with
+// 8 of 12 column-tiles large).  The activation epilogues stay on 128 x 128
+// tiles, where the other workgroup of the CU hides them; split-K and
+// grouped products use one tile size.
 template <int LAYOUT, int EPI, bool KCAT>
 static hipError_t pick(const GemmArgs &a, hipStream_t s) {
   const int64_t n = cus();
-  const int64_t t256 = ((a.M + 255) / 256) * ((a.N + 255) / 256) * a.splits * a.groups;
-  const int64_t t128 = ((a.M + 127) / 128) * ((a.N + 127) / 128) * a.splits * a.groups;
+  const int64_t tmb = (a.M + 255) / 256, tms = (a.M + 127) / 128;
+  const int64_t tnb = (a.N + 255) / 256;
   constexpr bool BIG_OK = EPI == EPI_STORE || EPI == EPI_STORE_F32;
   if constexpr (BIG_OK) {
-    const double big_rounds = (double)((t256 + n - 1) / n);
-    const double pair_rounds = 0.62 * (double)t128 / (double)(2 * n);
-    if (big_rounds < pair_rounds) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
+    const int64_t z = (int64_t)a.splits * a.groups;
+    int64_t best_c = 0;
+    double best = 1e30;
+    const int64_t cmax = z > 1 ? 0 : tnb - 1;  // split / grouped products: no column split
+    for (int64_t c = 0; c <= tnb; ++c) {
+      if (c > cmax && c < tnb) continue;
+      const int64_t rest = std::max<int64_t>(a.N - c * 256, 0);
+      const double cost = plan_cost(tmb * c * z, tms * ((rest + 127) / 128) * z, n);
+      if (cost < best - 1e-9) {
+        best = cost;
+        best_c = c;
+      }
+    }
+    if (best_c >= tnb) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
+    if (best_c > 0) {
+      const int64_t c0 = best_c * 256;
+      const hipError_t e = run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(single_cols<LAYOUT, EPI>(a, 0, c0), s);
+      if (e != hipSuccess) return e;
+      return run<128, 128, 2, 2, 2, 2, LAYOUT, EPI, KCAT>(single_cols<LAYOUT, EPI>(a, c0, a.N - c0), s);
+    }
   }
   return run<128, 128, 2, 2, 2, 2, LAYOUT, EPI, KCAT>(a, s);
 }

@@ -24,7 +24,10 @@ def _as(dtype, a):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("M,K,N", [(1, 8, 8), (37, 24, 40), (300, 56, 264), (2048, 64, 2048)])
+@pytest.mark.parametrize("M,K,N", [(1, 8, 8), (37, 24, 40), (300, 56, 264), (2048, 64, 2048),
+                                   # bf16: leading column-tiles on 256 x 256 tiles, the rest on
+                                   # 128 x 128 ones (8 of 12; 13 of 17 with ragged M and N)
+                                   (8192, 64, 3072), (3976, 64, 4104)])
 def test_col_linear_identity_act_exact(dtype, M, K, N):
     # |sum| <= 4K <= 256: exact in bf16 storage too
     note(f"col NN exact {dtype} {M}x{K}x{N}")
@@ -44,7 +47,9 @@ def test_col_linear_identity_act_exact(dtype, M, K, N):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("M,K,N", [(5, 16, 8), (129, 200, 136), (1024, 1032, 520), (4096, 256, 1024),
                                    # K % 64 == 0 and >= 64 tiles: the LDS-DMA kernel, ragged M / N
-                                   (1000, 640, 1352), (3000, 1024, 2056), (8192, 64, 1024)])
+                                   (1000, 640, 1352), (3000, 1024, 2056), (8192, 64, 1024),
+                                   # bf16: column-tiles split between 256 x 256 and 128 x 128 tiles
+                                   (3976, 256, 4104)])
 def test_row_partial_exact(dtype, M, K, N):
     note(f"row NN exact {dtype} {M}x{K}x{N}")
     rng = np.random.default_rng(7 * M + K)
