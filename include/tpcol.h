@@ -146,17 +146,20 @@ size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t
  * then K heads, then V heads, head t at offset t*d inside each block
  * ("Megatron-LM 实战 04", TPAttention: qkv reshaped to (3, heads, d)).
  * Causal: key j is visible to query i iff j <= i (within one sequence).
- *   X    [b*s x h]                      ldx    bf16 (token-major, batch-major)
- *   Wqkv [h x 3*heads_local*d]          ldwqkv bf16
- *   Wo   [heads_local*d x h]            ldwo   bf16
+ *   X    [b*s x h]                      ldx    dtype (token-major, batch-major)
+ *   Wqkv [h x 3*heads_local*d]          ldwqkv dtype
+ *   Wo   [heads_local*d x h]            ldwo   dtype
  *   P    [b*s x h]                      ldp    float32 (output)
  *   ws   tp_attn_heads_shard_workspace() bytes: QKV_i [b*s x 3*hl*d] then
- *        O_i [b*s x hl*d], both bf16 row-major, readable after the call,
+ *        O_i [b*s x hl*d], both dtype row-major, readable after the call,
  *        then each query row's softmax statistic (fp32 [b][hl][s], log2 of
  *        sum_j exp2(S_ij log2(e)) for the scaled scores S), which
  *        tp_attn_shard_backward reads.
- * Only TP_BF16 and d == 128 are supported (TP_ERR_DTYPE / TP_ERR_SHAPE);
- * 3*heads_local*d must not exceed 2^24 (TP_ERR_SHAPE).
+ * TP_BF16 with d == 128 runs the flash kernels; TP_F32, or any head dim
+ * 1..256, runs general kernels (fp32 softmax and accumulation either way;
+ * b*heads_local <= 65535 there).  d outside 1..256, or 3*heads_local*d above
+ * 2^24, is TP_ERR_SHAPE; heads_local*d*element size must be a multiple of 16
+ * bytes (TP_ERR_ALIGN).
  */
 int tp_attn_heads_shard(int dtype, int64_t b, int64_t s, int64_t h,
                         int64_t heads_local, int64_t d, int causal,
@@ -180,7 +183,7 @@ size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s,
  *   Wqkv [h x (heads_local + 2*kv_heads_local)*d]: Q heads, then K heads,
  *        then V heads, head u at offset u*d inside its block.
  *   ws   tp_attn_gqa_shard_workspace() bytes: QKV_i [b*s x (hl + 2*kvl)*d]
- *        then O_i [b*s x hl*d], bf16 row-major, readable after the call,
+ *        then O_i [b*s x hl*d], dtype row-major, readable after the call,
  *        then the per-row softmax statistic as for tp_attn_heads_shard.
  * heads_local must be a multiple of kv_heads_local, and
  * (heads_local + 2*kv_heads_local)*d at most 2^24 (TP_ERR_SHAPE); otherwise
@@ -211,17 +214,17 @@ size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t head
  *                                 dX_i = [dQ | dK | dV] Wqkv_i^T
  * dX_i is this shard's partial of dX = sum_i dX_i (f's backward all-reduce;
  * tp_shard_sum).
- *   X, Wqkv, Wo, dY: as in the forward call (bf16); dY [b*s x h] lddy.
+ *   X, Wqkv, Wo, dY: as in the forward call (dtype); dY [b*s x h] lddy.
  *   fwd_ws: the workspace of the forward call (tp_attn_heads_shard or
  *        tp_attn_gqa_shard) on the same inputs, as it left it: QKV_i, O_i
  *        and the row statistic are read, not recomputed.
  *   Outputs (float32, dense unless noted): dWqkv [h x (hl + 2*kvl)*d],
  *        dWo [hl*d x h], dXi [b*s x h] with row stride lddx.
- *   ws   tp_attn_shard_backward_workspace() bytes: dO_i (bf16), D (fp32),
- *        [dQ | dK | dV] (bf16, packed like QKV_i) and, for grouped-query
- *        shards whose kv heads alone would not fill the device, fp32 dK/dV
- *        partials of head subsets (added in a fixed order).
- * bf16 and d == 128 only; shape rules as for tp_attn_gqa_shard.  Both
+ *   ws   tp_attn_shard_backward_workspace() bytes: dO_i (dtype), D (fp32),
+ *        [dQ | dK | dV] (dtype, packed like QKV_i) and, for bf16 grouped-query
+ *        shards with d == 128 whose kv heads alone would not fill the device,
+ *        fp32 dK/dV partials of head subsets (added in a fixed order).
+ * dtype and shape rules as for tp_attn_gqa_shard.  Both
  * workspaces 256-byte aligned.  Every sum runs in a fixed order: repeated
  * calls give identical bits.
  */

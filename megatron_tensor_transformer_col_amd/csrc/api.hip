@@ -130,63 +130,84 @@ BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
   return w;
 }
 
-// forward workspace: packed QKV_i, O_i (bf16) and the per-row softmax
+// the flash kernels take bf16 with head dim 128; every other shape runs the
+// general attention kernels
+bool attn_fast(int dtype, int64_t d) { return dtype == TP_BF16 && d == 128; }
+
+// forward workspace: packed QKV_i, O_i (dtype) and the per-row softmax
 // statistic (fp32 [b][hl][s]) the backward reads
 struct AttnWs {
   size_t qkv, o, lse, total;
 };
-AttnWs attn_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
-  const size_t T = (size_t)b * (size_t)s;
+AttnWs attn_ws(int dtype, int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
+  const size_t T = (size_t)b * (size_t)s, e = esize(dtype);
   AttnWs w;
   w.qkv = 0;
-  w.o = round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
-  w.lse = w.o + round256(T * (size_t)hl * (size_t)d * 2);
+  w.o = round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * e);
+  w.lse = w.o + round256(T * (size_t)hl * (size_t)d * e);
   w.total = w.lse + round256(T * (size_t)hl * 4);
   return w;
 }
 
-// backward workspace: dO_i (bf16 [T x hl*d]), D (fp32 [b][hl][s]) and
-// dQKV_i (bf16, packed like QKV_i)
+// backward workspace: dO_i (dtype [T x hl*d]), D (fp32 [b][hl][s]),
+// dQKV_i (dtype, packed like QKV_i) and, for the flash kernels' split
+// grouped-query heads, fp32 dK / dV partials
 struct AttnBwdWs {
   size_t dO, D, dqkv, part, total;
 };
-AttnBwdWs attn_bwd_ws(int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
-  const size_t T = (size_t)b * (size_t)s;
+AttnBwdWs attn_bwd_ws(int dtype, int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d) {
+  const size_t T = (size_t)b * (size_t)s, e = esize(dtype);
   AttnBwdWs w;
   w.dO = 0;
-  w.D = round256(T * (size_t)hl * (size_t)d * 2);
+  w.D = round256(T * (size_t)hl * (size_t)d * e);
   w.dqkv = w.D + round256(T * (size_t)hl * 4);
-  w.part = w.dqkv + round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * 2);
-  w.total = w.part + round256(attn_bwd_part_bytes(b, s, hl, kvl));
+  w.part = w.dqkv + round256(T * (size_t)(hl + 2 * kvl) * (size_t)d * e);
+  w.total = w.part + (attn_fast(dtype, d) ? round256(attn_bwd_part_bytes(b, s, hl, kvl)) : 0);
   return w;
 }
 
 }  // namespace
 
 namespace {
-int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
-                     int64_t kv_heads_local, int64_t d, int causal, const void *X, int64_t ldx,
-                     const void *Wqkv, int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P,
-                     int64_t ldp, void *ws, size_t ws_bytes, void *stream) {
-  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports bf16 only");
-  TRY(check_dims({b, s_len, h, heads_local, kv_heads_local, d}, fn));
+// Shape rules of the attention entry points (after check_dims): head counts,
+// kv grouping, head dim (128 for the flash kernels' bf16 path, 1..256
+// otherwise), 16-byte rows of the packed Q|K|V and O buffers.
+int check_attn_shape(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local, int64_t kv_heads_local,
+                     int64_t d) {
   if (h < 1 || heads_local < 1) return fail(TP_ERR_SHAPE, "h and heads_local must be >= 1");
   if (kv_heads_local < 1 || heads_local % kv_heads_local)
     return fail(TP_ERR_SHAPE, "heads_local %lld is not a multiple of kv_heads_local %lld",
                 (long long)heads_local, (long long)kv_heads_local);
-  if (d != 128) return fail(TP_ERR_SHAPE, "head dim %lld unsupported (128 only)", (long long)d);
-  const int64_t T = b * s_len;
-  if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
-  const int64_t w = heads_local * d;
+  if (!attn_fast(dtype, d) && !attn_general_fits(s_len, d))
+    return fail(TP_ERR_SHAPE, "head dim %lld outside 1..256", (long long)d);
+  if (b * s_len > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
+  if (!attn_fast(dtype, d) && b * heads_local > 65535)
+    return fail(TP_ERR_SHAPE, "b*heads_local must be <= 65535 for head dim %lld", (long long)d);
   const int64_t wqkv = (heads_local + 2 * kv_heads_local) * d;
   if (wqkv > (int64_t(1) << 24))
     return fail(TP_ERR_SHAPE, "(heads_local + 2*kv_heads_local)*d must be <= 2^24");
-  TRY(check_mat(X, T, h, ldx, 2, "X"));
-  TRY(check_mat(Wqkv, h, wqkv, ldwqkv, 2, "Wqkv"));
-  TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));
+  if (((size_t)(heads_local * d) * esize(dtype)) % 16 != 0)
+    return fail(TP_ERR_ALIGN, "heads_local*d*element size must be a multiple of 16 bytes");
+  return TP_OK;
+}
+
+int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
+                     int64_t kv_heads_local, int64_t d, int causal, const void *X, int64_t ldx,
+                     const void *Wqkv, int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P,
+                     int64_t ldp, void *ws, size_t ws_bytes, void *stream) {
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
+  TRY(check_dims({b, s_len, h, heads_local, kv_heads_local, d}, fn));
+  TRY(check_attn_shape(dtype, b, s_len, h, heads_local, kv_heads_local, d));
+  const size_t e = esize(dtype);
+  const int64_t T = b * s_len;
+  const int64_t w = heads_local * d;
+  const int64_t wqkv = (heads_local + 2 * kv_heads_local) * d;
+  TRY(check_mat(X, T, h, ldx, e, "X"));
+  TRY(check_mat(Wqkv, h, wqkv, ldwqkv, e, "Wqkv"));
+  TRY(check_mat(Wo, w, h, ldwo, e, "Wo"));
   TRY(check_mat(P, T, h, ldp, 4, "P"));
   if (T == 0) return ok();
-  const AttnWs L = attn_ws(b, s_len, heads_local, kv_heads_local, d);
+  const AttnWs L = attn_ws(dtype, b, s_len, heads_local, kv_heads_local, d);
   if (ws == nullptr || ws_bytes < L.total)
     return fail(TP_ERR_WORKSPACE, "attention needs %zu workspace bytes, got %zu", L.total, ws_bytes);
   if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
@@ -198,7 +219,7 @@ int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, in
   float *lse = reinterpret_cast<float *>(base + L.lse);
 
   GemmArgs q;
-  q.dtype = DT_BF16;
+  q.dtype = dtype;
   q.layout = LAY_NN;
   q.epi = EPI_STORE;
   q.M = T; q.N = wqkv; q.K = h;
@@ -206,11 +227,16 @@ int attn_impl(const char *fn, int dtype, int64_t b, int64_t s_len, int64_t h, in
   q.B = Wqkv; q.ldb = ldwqkv;
   q.C = qkv; q.ldc = wqkv;
   TRY(hip_status(launch_gemm(q, st), "QKV GEMM"));
-  TRY(hip_status(launch_flash_attn(qkv, wqkv, O, w, lse, b, s_len, heads_local, kv_heads_local, d,
-                                   causal != 0, st),
-                 "attention"));
+  if (attn_fast(dtype, d))
+    TRY(hip_status(launch_flash_attn(qkv, wqkv, O, w, lse, b, s_len, heads_local, kv_heads_local, d,
+                                     causal != 0, st),
+                   "attention"));
+  else
+    TRY(hip_status(launch_attn_general(dtype, qkv, wqkv, O, w, lse, b, s_len, heads_local, kv_heads_local, d,
+                                       causal != 0, st),
+                   "attention"));
   GemmArgs o;
-  o.dtype = DT_BF16;
+  o.dtype = dtype;
   o.layout = LAY_NN;
   o.epi = EPI_STORE_F32;
   o.M = T; o.N = h; o.K = w;
@@ -227,29 +253,23 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
                   int64_t lddy, const void *fwd_ws, size_t fwd_ws_bytes, float *dWqkv, float *dWo,
                   float *dXi, int64_t lddx, void *ws, size_t ws_bytes, void *stream) {
   const char *fn = "tp_attn_shard_backward";
-  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "attention supports bf16 only");
+  if (!dtype_ok(dtype)) return fail(TP_ERR_DTYPE, "dtype %d", dtype);
   TRY(check_dims({b, s_len, h, heads_local, kv_heads_local, d}, fn));
-  if (h < 1 || heads_local < 1) return fail(TP_ERR_SHAPE, "h and heads_local must be >= 1");
-  if (kv_heads_local < 1 || heads_local % kv_heads_local)
-    return fail(TP_ERR_SHAPE, "heads_local %lld is not a multiple of kv_heads_local %lld",
-                (long long)heads_local, (long long)kv_heads_local);
-  if (d != 128) return fail(TP_ERR_SHAPE, "head dim %lld unsupported (128 only)", (long long)d);
+  TRY(check_attn_shape(dtype, b, s_len, h, heads_local, kv_heads_local, d));
+  const size_t e = esize(dtype);
   const int64_t T = b * s_len;
-  if (T > kMaxDim) return fail(TP_ERR_SHAPE, "b*s too large");
   const int64_t w = heads_local * d;
   const int64_t wqkv = (heads_local + 2 * kv_heads_local) * d;
-  if (wqkv > (int64_t(1) << 24))
-    return fail(TP_ERR_SHAPE, "(heads_local + 2*kv_heads_local)*d must be <= 2^24");
-  TRY(check_mat(X, T, h, ldx, 2, "X"));
-  TRY(check_mat(Wqkv, h, wqkv, ldwqkv, 2, "Wqkv"));
-  TRY(check_mat(Wo, w, h, ldwo, 2, "Wo"));
-  TRY(check_mat(dY, T, h, lddy, 2, "dY"));
+  TRY(check_mat(X, T, h, ldx, e, "X"));
+  TRY(check_mat(Wqkv, h, wqkv, ldwqkv, e, "Wqkv"));
+  TRY(check_mat(Wo, w, h, ldwo, e, "Wo"));
+  TRY(check_mat(dY, T, h, lddy, e, "dY"));
   TRY(check_mat(dWqkv, h, wqkv, wqkv, 4, "dWqkv"));
   TRY(check_mat(dWo, w, h, h, 4, "dWo"));
   TRY(check_mat(dXi, T, h, lddx, 4, "dXi"));
   if (dWqkv == nullptr || dWo == nullptr) return fail(TP_ERR_ARG, "dWqkv and dWo are required");
-  const AttnWs F = attn_ws(b, s_len, heads_local, kv_heads_local, d);
-  const AttnBwdWs L = attn_bwd_ws(b, s_len, heads_local, kv_heads_local, d);
+  const AttnWs F = attn_ws(dtype, b, s_len, heads_local, kv_heads_local, d);
+  const AttnBwdWs L = attn_bwd_ws(dtype, b, s_len, heads_local, kv_heads_local, d);
   if (T > 0) {
     if (fwd_ws == nullptr || fwd_ws_bytes < F.total)
       return fail(TP_ERR_WORKSPACE, "the forward's workspace (%zu bytes) is required, got %zu", F.total,
@@ -273,7 +293,7 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
   if (T > 0) {
     // dO_i = dY Wo_i^T  (row-parallel output projection, input gradient)
     GemmArgs a;
-    a.dtype = DT_BF16; a.layout = LAY_NT; a.epi = EPI_STORE;
+    a.dtype = dtype; a.layout = LAY_NT; a.epi = EPI_STORE;
     a.M = T; a.N = w; a.K = h;
     a.A = dY; a.lda = lddy;
     a.B = Wo; a.ldb = ldwo;
@@ -283,7 +303,7 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
   // dWo_i = O_i^T dY  (row-parallel weight gradient)
   {
     GemmArgs g;
-    g.dtype = DT_BF16; g.layout = LAY_TN; g.epi = EPI_STORE_F32;
+    g.dtype = dtype; g.layout = LAY_TN; g.epi = EPI_STORE_F32;
     g.M = w; g.N = h; g.K = T;
     g.A = O; g.lda = w;
     g.B = dY; g.ldb = lddy;
@@ -293,14 +313,18 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
     g.part = reinterpret_cast<float *>(dqkv); g.part_bytes = L.total - L.dqkv;
     TRY(hip_status(launch_gemm(g, st), "dWo GEMM"));
   }
-  if (T > 0)
+  if (T > 0 && attn_fast(dtype, d))
     TRY(hip_status(launch_attn_bwd(qkv, wqkv, O, w, lse, dO, w, Dr, dqkv, part, b, s_len, heads_local,
                                    kv_heads_local, d, causal != 0, st),
+                   "attention backward"));
+  else if (T > 0)
+    TRY(hip_status(launch_attn_bwd_general(dtype, qkv, wqkv, O, w, lse, dO, w, Dr, dqkv, b, s_len, heads_local,
+                                           kv_heads_local, d, causal != 0, st),
                    "attention backward"));
   // dWqkv_i = X^T dQKV_i  (column-parallel weight gradient)
   {
     GemmArgs g;
-    g.dtype = DT_BF16; g.layout = LAY_TN; g.epi = EPI_STORE_F32;
+    g.dtype = dtype; g.layout = LAY_TN; g.epi = EPI_STORE_F32;
     g.M = h; g.N = wqkv; g.K = T;
     g.A = X; g.lda = ldx;
     g.B = dqkv; g.ldb = wqkv;
@@ -310,7 +334,7 @@ int attn_bwd_impl(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_
   if (T > 0) {
     // dX_i = dQKV_i Wqkv_i^T  (this shard's partial of dX)
     GemmArgs x;
-    x.dtype = DT_BF16; x.layout = LAY_NT; x.epi = EPI_STORE_F32;
+    x.dtype = dtype; x.layout = LAY_NT; x.epi = EPI_STORE_F32;
     x.M = T; x.N = h; x.K = wqkv;
     x.A = dqkv; x.lda = wqkv;
     x.B = Wqkv; x.ldb = ldwqkv;
@@ -372,16 +396,14 @@ size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t
 
 size_t tp_attn_heads_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
                                      int64_t d) {
-  (void)dtype;
-  if (b < 0 || s < 0 || heads_local < 0 || d < 0) return 0;
-  return attn_ws(b, s, heads_local, heads_local, d).total;
+  if (!dtype_ok(dtype) || b < 0 || s < 0 || heads_local < 0 || d < 0) return 0;
+  return attn_ws(dtype, b, s, heads_local, heads_local, d).total;
 }
 
 size_t tp_attn_shard_backward_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
                                         int64_t kv_heads_local, int64_t d) {
-  (void)dtype;
-  if (b < 0 || s < 0 || heads_local < 0 || kv_heads_local < 0 || d < 0) return 0;
-  return attn_bwd_ws(b, s, heads_local, kv_heads_local, d).total;
+  if (!dtype_ok(dtype) || b < 0 || s < 0 || heads_local < 0 || kv_heads_local < 0 || d < 0) return 0;
+  return attn_bwd_ws(dtype, b, s, heads_local, kv_heads_local, d).total;
 }
 
 int tp_attn_shard_backward(int dtype, int64_t b, int64_t s, int64_t h, int64_t heads_local,
@@ -395,9 +417,8 @@ int tp_attn_shard_backward(int dtype, int64_t b, int64_t s, int64_t h, int64_t h
 
 size_t tp_attn_gqa_shard_workspace(int dtype, int64_t b, int64_t s, int64_t heads_local,
                                    int64_t kv_heads_local, int64_t d) {
-  (void)dtype;
-  if (b < 0 || s < 0 || heads_local < 0 || kv_heads_local < 0 || d < 0) return 0;
-  return attn_ws(b, s, heads_local, kv_heads_local, d).total;
+  if (!dtype_ok(dtype) || b < 0 || s < 0 || heads_local < 0 || kv_heads_local < 0 || d < 0) return 0;
+  return attn_ws(dtype, b, s, heads_local, kv_heads_local, d).total;
 }
 
 size_t tp_mlp_shard_backward_workspace(int dtype, int act, int64_t M, int64_t Ni) {

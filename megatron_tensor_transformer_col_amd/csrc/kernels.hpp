@@ -104,6 +104,17 @@ hipError_t launch_attn_bwd(const void *qkv, int64_t ldqkv, const void *O, int64_
                            const void *dO, int64_t lddo, float *Dr, void *dqkv, float *part, int64_t b, int64_t s,
                            int64_t heads_local, int64_t kv_heads_local, int64_t d, bool causal, hipStream_t st);
 size_t attn_bwd_part_bytes(int64_t b, int64_t s, int64_t heads_local, int64_t kv_heads_local);
+// The same two steps for any other shape: fp32 (DT_F32) or bf16 operands,
+// head dim 1..256 (attn_general_fits), same packing, lse and D conventions;
+// SIMT kernels, no scratch.
+bool attn_general_fits(int64_t s, int64_t d);
+hipError_t launch_attn_general(int dtype, const void *qkv, int64_t ldqkv, void *O, int64_t ldo, float *lse,
+                               int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d, bool causal,
+                               hipStream_t st);
+hipError_t launch_attn_bwd_general(int dtype, const void *qkv, int64_t ldqkv, const void *O, int64_t ldo,
+                                   const float *lse, const void *dO, int64_t lddo, float *Dr, void *dqkv,
+                                   int64_t b, int64_t s, int64_t hl, int64_t kvl, int64_t d, bool causal,
+                                   hipStream_t st);
 
 // db[n] = sum_m dZ[m][n] (dZ dtype, db float32).
 hipError_t launch_rs_layernorm(int out_dtype, int64_t rows, int64_t N, int n, const float *const *parts,

@@ -68,6 +68,13 @@ def test_workspace_sizes():
     assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 8, 128) == T * 1024 * 2 + T * 8 * 4 + T * 24 * 128 * 2
     assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 128) == (
         T * 1024 * 2 + T * 8 * 4 + T * 12 * 128 * 2 + 4 * T * 2 * 2 * 128 * 4)
+    # fp32 / other head dims (general kernels): element size 4, no head-split partials
+    t = 2 * 10
+    r = lambda x: (x + 255) // 256 * 256
+    assert tp.tp_attn_heads_shard_workspace(0, 2, 10, 4, 16) == r(t * 12 * 16 * 4) + r(t * 64 * 4) + r(t * 4 * 4)
+    assert tp.tp_attn_shard_backward_workspace(0, 2, 10, 4, 4, 16) == r(t * 64 * 4) + r(t * 4 * 4) + r(t * 12 * 16 * 4)
+    assert tp.tp_attn_shard_backward_workspace(1, 4, 2048, 8, 2, 64) == T * 512 * 2 + T * 8 * 4 + T * 12 * 64 * 2
+    assert tp.tp_attn_heads_shard_workspace(7, 2, 10, 4, 16) == 0  # unknown dtype
     # backward: dH, a dH-sized partial region, H, dZ and 64 fp32 rows of db1
     # column-sum partials (GELU) /
     # dH, H, [dZg | dZu] (SwiGLU, no bias)
@@ -158,10 +165,14 @@ def test_col_linear_noalloc_validation(case, expect):
 def test_attention_validation():
     lib = tp.lib()
     f = lib.tp_attn_heads_shard
-    # fp32 is not supported
-    assert f(0, 4, 2048, 4096, 8, 128, 1, A, 4096, A, 3072, A, 4096, A, 4096, A, 1 << 30, None) == -4
-    # head dim other than 128
-    assert f(1, 4, 2048, 4096, 8, 64, 1, A, 4096, A, 1536, A, 4096, A, 4096, A, 1 << 30, None) == -2
+    # unknown dtype
+    assert f(5, 4, 2048, 4096, 8, 128, 1, A, 4096, A, 3072, A, 4096, A, 4096, A, 1 << 30, None) == -4
+    # head dim beyond 256 (fp32 and other head dims run the general kernels)
+    assert f(1, 4, 2048, 4096, 8, 300, 1, A, 4096, A, 7200, A, 4096, A, 4096, A, 1 << 30, None) == -2
+    # fp32, 1 head of 3: the 12-byte O rows are not 16-byte multiples
+    assert f(0, 1, 16, 64, 1, 3, 1, A, 64, A, 12, A, 64, A, 64, A, 1 << 30, None) == -3
+    # fp32 head dim 16 (the pages' example shape): workspace too small
+    assert f(0, 2, 10, 128, 4, 16, 1, A, 128, A, 192, A, 128, A, 128, A, 1024, None) == -5
     # workspace too small
     assert f(1, 4, 2048, 4096, 8, 128, 1, A, 4096, A, 3072, A, 4096, A, 4096, A, 1024, None) == -5
     # Wqkv narrower than 3 * heads_local * d
@@ -249,9 +260,9 @@ def test_attention_backward_validation():
         return g(dt, 4, 2048, 4096, hl, kvl, d, 1, X, 4096, A, ldwqkv, A, 4096, A, 4096, fws, fwn, dWqkv, dWo, dX,
                  4096, ws, wsn, None)
 
-    assert call(dt=0) == -4                        # fp32 attention is not supported
+    assert call(dt=3) == -4                        # unknown dtype
     assert call(kvl=3) == -2                       # 8 query heads do not group over 3 kv heads
-    assert call(d=64) == -2                        # head dim 128 only
+    assert call(d=300) == -2                       # head dim 1..256
     assert call(ldwqkv=1024) == -2                 # ld < (hl + 2 kvl) d
     assert call(X=None) == -1
     assert call(dWo=None) == -1
