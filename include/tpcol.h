@@ -377,7 +377,9 @@ int tp_check_split(int64_t h, int64_t ffn, int64_t heads, int64_t n);
 
 /* Tuning/testing option: token count at or below which the linear calls take
  * the decode GEMV path (default 16, range 0..16; 0 disables the GEMV path).
- * Process-wide; returns the previous value, or TP_ERR_ARG if out of range. */
+ * Process-wide; returns the previous value, or TP_ERR_ARG if out of range.
+ * The environment variable TPCOL_GEMV_MAX_M (an integer 0..16), read when the
+ * library loads, sets the initial value. */
 int tp_set_gemv_max_m(int max_m);
 
 /* Static description of a status code.  Never NULL. */

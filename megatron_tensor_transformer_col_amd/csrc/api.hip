@@ -5,6 +5,7 @@
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/tpcol.h"
@@ -15,7 +16,17 @@ using namespace tpcol;
 namespace {
 
 thread_local char g_err[512] = "";
-std::atomic<int> g_gemv_max_m{16};
+
+// Initial GEMV threshold: TPCOL_GEMV_MAX_M from the environment when the
+// library loads (an integer 0..16; anything else keeps the default 16).
+int initial_gemv_max_m() {
+  const char *v = getenv("TPCOL_GEMV_MAX_M");
+  if (v == nullptr || *v == '\0') return 16;
+  char *end = nullptr;
+  const long m = strtol(v, &end, 10);
+  return (*end == '\0' && m >= 0 && m <= 16) ? (int)m : 16;
+}
+std::atomic<int> g_gemv_max_m{initial_gemv_max_m()};
 
 int fail(int status, const char *fmt, ...) {
   va_list ap;

@@ -44,6 +44,19 @@ def test_check_split_matches_divisibility(h, ffn, heads, n):
     assert (tp.tp_check_split(h, ffn, heads, n) == 0) == ok
 
 
+@pytest.mark.parametrize("env,expect", [("4", 4), ("0", 0), ("17", 16), ("x", 16)])
+def test_gemv_threshold_environment(env, expect):
+    # TPCOL_GEMV_MAX_M sets the initial threshold when the library loads
+    import subprocess
+    import sys
+    code = ("import megatron_tensor_transformer_col_amd as tp; "
+            "print(tp.tp_set_gemv_max_m(16))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=120,
+                       env=dict(os.environ, TPCOL_GEMV_MAX_M=env))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert int(r.stdout.split()[-1]) == expect
+
+
 def test_gemv_threshold_option():
     prev = tp.tp_set_gemv_max_m(8)
     try:
