@@ -274,3 +274,54 @@ def test_mlp_backward_repeats_bitwise(h, ffn):
     for r in runs[1:]:
         for k in r:
             assert T.equal(r[k], runs[0][k]), k
+
+
+@pytest.mark.parametrize("act,h,ffn", [("gelu", 512, 512), ("swiglu", 256, 512)])
+def test_mlp_backward_graph_replays(act, h, ffn):
+    # a captured backward call (recompute, paired split-K weight gradients
+    # and their sums, db1, dX) replays to the eager call's bits, with eager
+    # calls and workspace clobbering in between
+    note(f"bf16 MLP {act} bwd graph replay 4096x{h}x{ffn}")
+    T = torch()
+    if act == "gelu":
+        d = synth.make_mlp_inputs(4096, h, ffn, "bf16", seed=6, with_dy=True, with_bias=True)
+        W1, W2 = dev(d["W1"]), dev(d["W2"])
+        kw = dict(b1=dev(d["b1"])[0])
+    else:
+        d = synth.make_swiglu_inputs(4096, h, ffn, "bf16", seed=6, with_dy=True)
+        W1, W2 = dev(d["Wg"]), dev(d["Wd"])
+        kw = dict(Wup=dev(d["Wu"]))
+    X, dY = dev(d["X"]), dev(d["dY"])
+    code = tp.TP_ACT_GELU_ERF if act == "gelu" else tp.TP_ACT_SWIGLU
+    ws = T.empty((tp.tp_mlp_shard_backward_workspace(tp.TP_BF16, code, 4096, ffn),), dtype=T.uint8, device="cuda:0")
+    o = {"dW1": empty((h, ffn), "f32"), "dW2": empty((ffn, h), "f32"), "dX": empty((4096, h), "f32")}
+    if act == "gelu":
+        o["db1"] = empty((1, ffn), "f32")
+        kw["db1"] = o["db1"][0]
+    else:
+        o["dWu"] = empty((h, ffn), "f32")
+        kw["dWup"] = o["dWu"]
+
+    def call():
+        tp.tp_mlp_shard_backward(X, W1, W2, dY, o["dW1"], o["dW2"], o["dX"], act=act, ws=ws, **kw)
+
+    call()
+    T.cuda.synchronize()
+    ref = {k: v.clone() for k, v in o.items()}
+    g = T.cuda.CUDAGraph()
+    with T.cuda.graph(g):
+        call()
+    T.cuda.synchronize()
+    for it in range(3):
+        for v in o.values():
+            v.fill_(float("nan"))
+        ws.fill_(it * 37)
+        T.cuda.synchronize()
+        g.replay()
+        T.cuda.synchronize()
+        for k in o:
+            assert T.equal(o[k], ref[k]), (it, k)
+        call()
+        T.cuda.synchronize()
+        for k in o:
+            assert T.equal(o[k], ref[k]), (it, "eager", k)
