@@ -251,7 +251,8 @@ def other_rooflines(torch, tp):
         "bound": "mfma", "kernel": "column dual GEMM + SwiGLU epilogue (8192 x 4096 x 2 x 3584)",
         "achieved": round(fl / ms / 1e9, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4), "avg_launch_us": round(ms * 1e3, 2),
-        "flops_per_launch": fl, "traffic": None}
+        "flops_per_launch": fl, "traffic": traffic_record(DUAL_TRAFFIC_PROFILE, TRAFFIC_SOURCES),
+        "traffic_unit": "HBM bytes per call (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"}
     del s
     s = R.decode()
     it = [0]
@@ -268,7 +269,10 @@ def other_rooflines(torch, tp):
         "bound": "hbm", "kernel": "decode column GEMV (split-K pass + finalize, 16 x 8192 x 3584, GELU)",
         "achieved": round(wb / ms / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": round(wb / ms / 1e6 / PEAK_HBM_GBS, 4), "avg_call_us": round(ms * 1e3, 2),
-        "weight_bytes_per_call": wb, "noalloc_avg_call_us": round(ms_na * 1e3, 2), "traffic": None}
+        "weight_bytes_per_call": wb, "noalloc_avg_call_us": round(ms_na * 1e3, 2),
+        "traffic": traffic_record(GEMV_TRAFFIC_PROFILE, GEMV_TRAFFIC_SOURCES),
+        "traffic_unit": "HBM bytes per call, split-K pass + finalize (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                        "copy-calibrated)"}
     return out
 
 
@@ -676,19 +680,28 @@ def run_op(torch, tp, synth, name, iters):
 # --------------------------------------------------------------------------- HBM traffic
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_col_gelu_gpt2m_shard.md")
 TRAFFIC_SOURCES = ["gemm_k64.hip", "gemm_common.hpp", "device_common.hpp", "lds_dma.hpp"]
+DUAL_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemm_swiglu_llama_shard.md")
+GEMV_TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "gemv_decode_mlp_shard.md")
+GEMV_TRAFFIC_SOURCES = ["gemv.hip", "device_common.hpp", "lds_dma.hpp"]
 
 
 def col_gemm_traffic():
     """HBM bytes per launch of the column GEMM from the committed rocprofv3
-    FETCH_SIZE / WRITE_SIZE record (KiB per dispatch, scaled by the factors a
-    1 GiB copy gave), or None when the record is missing or the kernel's
-    sources changed since the counters were taken."""
+    FETCH_SIZE / WRITE_SIZE record, or None (see traffic_record)."""
+    return traffic_record(TRAFFIC_PROFILE, TRAFFIC_SOURCES)
+
+
+def traffic_record(profile, sources):
+    """HBM bytes per call from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record (KiB per call, summed over the call's dispatches, scaled by the
+    factors a 1 GiB copy gave), or None when the record is missing or the
+    kernel's sources changed since the counters were taken."""
     import hashlib
     try:
-        line = next(l for l in open(TRAFFIC_PROFILE) if l.startswith("traffic-record:"))
+        line = next(l for l in open(profile) if l.startswith("traffic-record:"))
         rec = json.loads(line.split(":", 1)[1])
         h = hashlib.sha256()
-        for f in TRAFFIC_SOURCES:
+        for f in sources:
             with open(os.path.join(ROOT, "megatron_tensor_transformer_col_amd", "csrc", f), "rb") as fh:
                 h.update(fh.read())
     except (OSError, StopIteration, ValueError):
