@@ -140,7 +140,10 @@ def test_mlp_gelu_bf16_medium(T_, h, ffn, n):
                                         # 4 K-range splits each, one launch adds both
                                         (4096, 512, 512, 1),
                                         # the GPT-2-medium shard's shapes (h 1024, ffn 1024)
-                                        (8192, 1024, 1024, 1)])
+                                        (8192, 1024, 1024, 1),
+                                        # ragged [1032 x 1032] weight gradients in one launch,
+                                        # 2 K-range splits each
+                                        (8192, 1032, 1032, 1)])
 def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
     note(f"bf16 MLP GELU bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_mlp_inputs(T_, h, ffn, "bf16", seed=2, with_dy=True, with_bias=True)
@@ -159,7 +162,10 @@ def test_mlp_gelu_bf16_backward_medium(T_, h, ffn, n):
 # 128 x 128 output tiles only, 256 x 128 ones only, and 15 column-tiles of
 # 256 x 128 followed by 128 x 128 ones
 @pytest.mark.parametrize("T_,h,ffn,n", [(300, 264, 1056, 2), (520, 256, 2048, 1), (1024, 1024, 2048, 2),
-                                        (1100, 256, 2048, 1), (2100, 512, 2064, 1), (4200, 256, 2056, 1)])
+                                        (1100, 256, 2048, 1), (2100, 512, 2064, 1), (4200, 256, 2056, 1),
+                                        # the K-concatenated dX [3976 x 4104]: 13 of its 17 column-tiles
+                                        # on 256 x 256 tiles, the rest on 128 x 128 ones
+                                        (3976, 4104, 512, 1)])
 def test_mlp_swiglu_bf16_medium(T_, h, ffn, n):
     note(f"bf16 SwiGLU fwd+bwd {T_}x{h}x{ffn} n={n}")
     d = synth.make_swiglu_inputs(T_, h, ffn, "bf16", seed=3, with_dy=True)
