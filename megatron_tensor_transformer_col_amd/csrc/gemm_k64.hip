@@ -1,4 +1,4 @@
-// bf16 MFMA GEMM for gfx950 with 64-deep K slabs, four waves per workgroup.
+// bf16 MFMA GEMM for gfx950 with 64-deep K slabs.
 //
 //   C[M x N] = A[M x K] . B[K x N]   (fp32 accumulate, K a multiple of 64)
 //
@@ -9,19 +9,26 @@
 //    per slab, a whole cache line, so every L2 request of the HBM -> LDS DMA
 //    carries a full line; with 32-deep slabs half of them were 64-byte
 //    half-lines and the DMA topped out near 18 TB/s instead of ~23.
-//  * Four wave64 per workgroup (one per SIMD) with large per-wave tiles
-//    (64 x 64 or 128 x 128), accumulators in AGPRs.  The next 32-deep chunk's
-//    fragments are read from LDS while the current chunk's MFMAs run
-//    (two register sets), and one barrier per slab sits between a slab's two
-//    chunks, where every wave has finished reading the slab before.
-//  * 128 x 128 tiles run two workgroups per CU: while one is in its
-//    epilogue (activation, staging, stores) the other keeps the matrix cores
-//    busy, which hides the erf-GELU of the column-parallel product.  256 x 256
-//    tiles (one workgroup per CU) serve products with whole rounds of them.
+//  * 128 x 128 tiles: four wave64 per workgroup (one per SIMD, 64 x 64
+//    each) and two workgroups per CU.  The next 32-deep chunk's fragments
+//    are read from LDS while the current chunk's MFMAs run (two register
+//    sets), and one barrier per slab sits between a slab's two chunks,
+//    where every wave has finished reading the slab before.  While one
+//    workgroup is in its epilogue (activation, staging, stores) the other
+//    keeps the matrix cores busy, which hides the erf-GELU of the
+//    column-parallel product.
+//  * 256-row tiles (256 x 256, and the 128-row dual tiles): eight waves,
+//    two per SIMD, in ping-pong: the two waves of a SIMD alternate between
+//    a phase of MFMAs on fragments already in registers and a phase of LDS
+//    reads (and DMA issue), switching at workgroup barriers, so the matrix
+//    core of every SIMD always has one wave feeding it.  One workgroup per
+//    CU; these tiles serve products with whole rounds of them.
 //  * Dual products (SwiGLU: X.Wg and X.Wu) stage both weight slabs side by
 //    side and keep both accumulators of an output element in one wave, so
 //    the gate and up values meet in registers: 256 x 128 output tiles carry
 //    the same per-slab traffic and MFMA work as a 256 x 256 single product.
+//    A K-concatenated B (NT) keeps four waves on its 256 x 256 tiles: its
+//    second set of DMA offsets does not fit two waves' registers per SIMD.
 //  * The compiler's register allocation is steered with the minimal-register
 //    scheduling strategy (build flag); the default one shuffled accumulators
 //    between AGPRs and VGPRs inside the loop.
@@ -45,7 +52,16 @@ namespace tpcol {
 namespace k64 {
 
 constexpr int LBK = 64;  // slab depth
-constexpr int NW = 4;    // waves per workgroup
+constexpr int NW = 4;    // waves per workgroup (one per SIMD); eight in the ping-pong kernel
+
+// Workgroup barrier that the compiler may not schedule any instruction
+// across (the ping-pong loop relies on the MFMAs and LDS reads of a phase
+// staying between its two barriers).
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // device-scope (write-through) 16-byte store from LDS; see gemm_lds.hip
 typedef unsigned int u32x4_wt __attribute__((ext_vector_type(4)));
@@ -59,20 +75,20 @@ __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 // m/n-contiguous rows: granule index bits 1..3 XOR-ed with row bits
 __device__ __forceinline__ int swz_mn(int r) { return ((r & 3) | (((r >> 3) & 1) << 2)) << 1; }
 
-// DMA of a k-contiguous operand slab: ROWS rows x 64 k (8 rows per KiB).
-// Per-lane 32-bit offsets relative to the tile's first row; the slab's
-// base pointer is wave-uniform (SGPRs).  KCAT: rows of the second source
-// (k >= K1) have their own offsets.
-template <int ROWS, bool KCAT>
+// DMA of a k-contiguous operand slab: ROWS rows x 64 k (8 rows per KiB),
+// shared by NWI waves.  Per-lane 32-bit offsets relative to the tile's
+// first row; the slab's base pointer is wave-uniform (SGPRs).  KCAT: rows
+// of the second source (k >= K1) have their own offsets.
+template <int ROWS, bool KCAT, int NWI>
 struct KDma {
-  static constexpr int PER_WAVE = ROWS / 8 / NW;
-  static_assert(ROWS % (8 * NW) == 0, "rows");
+  static constexpr int PER_WAVE = ROWS / 8 / NWI;
+  static_assert(ROWS % (8 * NWI) == 0, "rows");
   uint32_t off[PER_WAVE];
   uint32_t off2[KCAT ? PER_WAVE : 1];
   __device__ __forceinline__ void init(int64_t ld, int64_t ld2, int row0, int rows_lim, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int row = (wave + NW * j) * 8 + lane / 8;
+      const int row = (wave + NWI * j) * 8 + lane / 8;
       const int c = (lane % 8) ^ swz_k(row);
       const int64_t gr = min(row0 + row, rows_lim - 1) - row0;
       off[j] = (uint32_t)(gr * ld * 2 + c * 16);
@@ -83,23 +99,23 @@ struct KDma {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const uint32_t o = (KCAT && second) ? off2[KCAT ? j : 0] : off[j];
-      dma16s(o, base, lds + (wave + NW * j) * 1024);
+      dma16s(o, base, lds + (wave + NWI * j) * 1024);
     }
   }
 };
 
-// DMA of an m/n-contiguous operand slab: 64 k-rows x COLS.
-template <int COLS>
+// DMA of an m/n-contiguous operand slab: 64 k-rows x COLS, shared by NWI waves.
+template <int COLS, int NWI>
 struct NDma {
   static constexpr int GPR = COLS / 8;    // granules per row
   static constexpr int RPB = 64 / GPR;    // rows per KiB
-  static constexpr int PER_WAVE = LBK / RPB / NW;
-  static_assert(GPR >= 16 && (LBK / RPB) % NW == 0, "cols");
+  static constexpr int PER_WAVE = LBK / RPB / NWI;
+  static_assert(GPR >= 16 && (LBK / RPB) % NWI == 0, "cols");
   uint32_t off[PER_WAVE];
   __device__ __forceinline__ void init(int64_t ld, int col0, int col_lim, int wave, int lane) {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int row = (wave + NW * j) * RPB + lane / GPR;
+      const int row = (wave + NWI * j) * RPB + lane / GPR;
       const int lg = (lane % GPR) ^ swz_mn(row);
       const int col = min(col0 + lg * 8, col_lim - 8) - col0;
       off[j] = (uint32_t)((int64_t)row * ld * 2 + col * 2);
@@ -107,7 +123,7 @@ struct NDma {
   }
   __device__ __forceinline__ void issue(const uint16_t *base, uint32_t lds, int wave) {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) dma16s(off[j], base, lds + (wave + NW * j) * 1024);
+    for (int j = 0; j < PER_WAVE; ++j) dma16s(off[j], base, lds + (wave + NWI * j) * 1024);
   }
 };
 
@@ -147,17 +163,19 @@ struct FragAddr {
   }
 };
 
-// BM x BN tile per workgroup of 4 waves (WGM x WGN), STAGES-deep ring of
-// 64-deep slabs, OCC workgroups per CU.
+// BM x BN tile per workgroup of NWV waves (WGM x WGN), STAGES-deep ring of
+// 64-deep slabs, OCC workgroups per CU.  NWV = 8: two waves per SIMD in
+// alternation (the ping-pong loop below).
 // DUAL (NN only): two products X.B and X.B2 of the same output tile, B's
 // and B2's slabs side by side in the stage (BN = twice the output width);
 // each wave holds both accumulators of its output columns, so the SwiGLU
 // epilogues pair them in registers.
-template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT, bool DUAL>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OCC, OCC)))
+template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT, bool DUAL,
+          int NWV>
+__global__ void __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(OCC * NWV / 4, OCC * NWV / 4)))
 gemm_k64_kernel(GemmParams pin) {
   GemmParams p = pin;
-  static_assert(WGM * WGN == NW, "4 waves");
+  static_assert(WGM * WGN == NWV && (NWV == 4 || (NWV == 8 && STAGES == 2 && OCC == 1)), "waves");
   static_assert(!DUAL || (LAYOUT == LAY_NN && !KCAT), "dual products are NN");
   constexpr int BNO = DUAL ? BN / 2 : BN;  // output tile width
   constexpr int WTM = BM / WGM, WTNO = BNO / WGN;
@@ -167,8 +185,8 @@ gemm_k64_kernel(GemmParams pin) {
   constexpr int A_EL = BM * LBK, B_EL = BN * LBK;
   constexpr int STAGE = A_EL + B_EL;  // elements
   constexpr int B2_OFF = BNO * LBK * 2;  // byte offset of B2's slab after B's (dual)
-  using ADma = typename std::conditional<AK, KDma<BM, false>, NDma<BM>>::type;
-  using BDma = typename std::conditional<BK, KDma<BNO, KCAT>, NDma<BNO>>::type;
+  using ADma = typename std::conditional<AK, KDma<BM, false, NWV>, NDma<BM, NWV>>::type;
+  using BDma = typename std::conditional<BK, KDma<BNO, KCAT, NWV>, NDma<BNO, NWV>>::type;
   constexpr int LOADS = ADma::PER_WAVE + (DUAL ? 2 : 1) * BDma::PER_WAVE;  // DMA ops per wave per slab
   static_assert(STAGES >= 2 && LOADS * STAGES < 64, "pipeline depth");
 
@@ -227,26 +245,27 @@ gemm_k64_kernel(GemmParams pin) {
   const int64_t bstep = BK ? LBK : (int64_t)LBK * p.ldb;
   const int64_t b2step = (int64_t)LBK * p.ldb2;  // dual
 
+  const int dw = wave;  // every wave issues its share of each slab's DMA
   ADma da;
   BDma db, db2;
-  if constexpr (AK) da.init(p.lda, 0, m0, M, wave, lane);
-  else da.init(p.lda, m0, M, wave, lane);
-  if constexpr (BK) db.init(p.ldb, p.ldb2, n0, N, wave, lane);
-  else db.init(p.ldb, n0, N, wave, lane);
-  if constexpr (DUAL) db2.init(p.ldb2, n0, N, wave, lane);
+  if constexpr (AK) da.init(p.lda, 0, m0, M, dw, lane);
+  else da.init(p.lda, m0, M, dw, lane);
+  if constexpr (BK) db.init(p.ldb, p.ldb2, n0, N, dw, lane);
+  else db.init(p.ldb, n0, N, dw, lane);
+  if constexpr (DUAL) db2.init(p.ldb2, n0, N, dw, lane);
 
   const uint32_t sbase = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(TP_AS3 const void *)smem);
   auto issue = [&](int kt, int stage) {
     const uint32_t base = sbase + stage * (STAGE * 2);
-    if constexpr (AK) da.issue(Ab + kt * astep, false, base, wave);
-    else da.issue(Ab + kt * astep, base, wave);
+    if constexpr (AK) da.issue(Ab + kt * astep, false, base, dw);
+    else da.issue(Ab + kt * astep, base, dw);
     if constexpr (BK) {
       const int k0 = kt * LBK;
       const bool second = KCAT && k0 >= p.K1;
-      db.issue(second ? B2b + (k0 - p.K1) : Bb + k0, second, base + A_EL * 2, wave);
+      db.issue(second ? B2b + (k0 - p.K1) : Bb + k0, second, base + A_EL * 2, dw);
     } else {
-      db.issue(Bb + kt * bstep, base + A_EL * 2, wave);
-      if constexpr (DUAL) db2.issue(B2b + kt * b2step, base + A_EL * 2 + B2_OFF, wave);
+      db.issue(Bb + kt * bstep, base + A_EL * 2, dw);
+      if constexpr (DUAL) db2.issue(B2b + kt * b2step, base + A_EL * 2 + B2_OFF, dw);
     }
   };
 
@@ -322,20 +341,62 @@ gemm_k64_kernel(GemmParams pin) {
     interleave();
   };
 
+  if constexpr (NWV == 4) {
 #pragma unroll
-  for (int s = 0; s < STAGES; ++s)
-    if (s < nk) issue(s, s);
-  if (nk >= STAGES) wait_vmcnt<LOADS * (STAGES - 1)>();
-  else wait_vmcnt<0>();
-  __syncthreads();
-  Frags F0, F1;
-  load_chunk(F0, 0, 0);
-  for (int kt = 0; kt < nk - 1; ++kt) {
-    half0(kt, F0, F1);
-    half1(kt, F1, F0);
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s, s);
+    if (nk >= STAGES) wait_vmcnt<LOADS * (STAGES - 1)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    Frags F0, F1;
+    load_chunk(F0, 0, 0);
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      half0(kt, F0, F1);
+      half1(kt, F1, F0);
+    }
+    half0(nk - 1, F0, F1);
+    mma(F1);
+  } else {
+    // Ping-pong: waves w and w + 4 share a SIMD.  Group 0 (waves 0..3)
+    // starts one phase ahead of group 1, and every phase ends at a
+    // workgroup barrier, so while one wave of a SIMD runs the MFMAs of a
+    // 32-deep chunk (its fragments already in registers) the other reads
+    // its fragments of the next chunk from LDS.  Chunk c = 2 kt + h is read
+    // in phase 2c by group 0 and 2c + 1 by group 1.  Each wave issues an
+    // eighth of every slab's DMA at the start of its read phase of the
+    // slab's first chunk: slab kt + 1 goes into the stage of slab kt - 1 in
+    // phases 4 kt (group 0) and 4 kt + 1 (group 1) -- slab kt - 1 was last
+    // read in phase 4 kt - 1 and every reader waited for its reads before
+    // that phase's barrier -- and every wave waits for its share before the
+    // barrier that ends phase 4 kt + 3.  (Issuing a whole slab from one
+    // group stalled that group's read phase behind the DMA queue: 10%
+    // slower; issuing inside the MFMA phases stalled the MFMAs: 7%.)
+    const bool g0 = wave < NW;
+    issue(0, 0);
+    if (nk > 1) {
+      issue(1, 1);
+      wait_vmcnt<LOADS>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    phase_barrier();
+    if (!g0) phase_barrier();  // group 1 one phase behind
+    Frags F;
+    for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 0 && kt >= 1 && kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+        load_chunk(F, kt & 1, h);
+        if (h == 1 && !g0 && kt + 1 < nk) wait_vmcnt<0>();
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        phase_barrier();
+        mma(F);
+        if (h == 1 && g0 && kt + 1 < nk) wait_vmcnt<0>();
+        phase_barrier();
+      }
+    }
+    if (g0) phase_barrier();  // as many barriers as group 1
   }
-  half0(nk - 1, F0, F1);
-  mma(F1);
 
   // ---- epilogue: lane holds C[row][col .. col+3] of every 16x16 tile
   const int g = lane >> 4, l16 = lane & 15;
@@ -370,7 +431,7 @@ gemm_k64_kernel(GemmParams pin) {
       }
     }
     __syncthreads();
-    for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+    for (int c = threadIdx.x; c < BM * CPR; c += NWV * 64) {
       const int rl = c / CPR, cc = c % CPR;
       const int row = m0 + rl, col = n0 + cc * (16 / OES);
       if (row < M && col < N)
@@ -401,7 +462,7 @@ gemm_k64_kernel(GemmParams pin) {
       }
     }
     __syncthreads();  // every wave is done reading the ring
-    for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+    for (int c = threadIdx.x; c < BM * CPR; c += NWV * 64) {
       const int rl = c / CPR, cc = c % CPR;
       const int row = m0 + rl, col = n0 + cc * 8;
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
@@ -439,7 +500,7 @@ gemm_k64_kernel(GemmParams pin) {
       // dZ (dZg) -> C, H -> C2, dZu -> C3
       void *C = which == 0 ? p.C : (which == 1 ? p.C2 : p.C3);
       const int64_t ldc = which == 0 ? p.ldc : (which == 1 ? p.ldc2 : p.ldc3);
-      for (int c = threadIdx.x; c < BM * CPR; c += NW * 64) {
+      for (int c = threadIdx.x; c < BM * CPR; c += NWV * 64) {
         const int rl = c / CPR, cc = c % CPR;
         const int row = m0 + rl, col = n0 + cc * 8;
         if (row < M && col < N)
@@ -467,7 +528,7 @@ gemm_k64_kernel(GemmParams pin) {
 
 // ---------------------------------------------------------------- host side
 template <int BM, int BN, int WGM, int WGN, int STAGES, int OCC, int LAYOUT, int EPI, bool KCAT,
-          bool DUAL = false>
+          bool DUAL = false, int NWV = 4>
 static hipError_t run(const GemmArgs &a, hipStream_t s) {
   constexpr int BNO = DUAL ? BN / 2 : BN;
   GemmParams p;
@@ -485,8 +546,8 @@ static hipError_t run(const GemmArgs &a, hipStream_t s) {
   p.zstride = a.zstride;
   p.A2 = a.A2; p.lda2 = a.lda2;
   p.zsplit = a.splits;
-  hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT, DUAL>),
-                     dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)(a.splits * a.groups)), dim3(NW * 64), 0, s,
+  hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT, DUAL, NWV>),
+                     dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)(a.splits * a.groups)), dim3(NWV * 64), 0, s,
                      p);
   return hipGetLastError();
 }
@@ -529,6 +590,14 @@ static double plan_cost(int64_t big_tiles, int64_t small_tiles, int64_t n) {
   return big + 0.62 * small + (big_tiles > 0 && small_tiles > 0 ? 0.17 : 0.0);
 }
 
+// 256 x 256 tiles: eight waves in ping-pong; a K-concatenated B keeps four
+// (its second set of DMA offsets does not fit two waves' registers per SIMD)
+template <int LAYOUT, int EPI, bool KCAT>
+static hipError_t run_big(const GemmArgs &a, hipStream_t s) {
+  if constexpr (KCAT) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
+  else return run<256, 256, 2, 4, 2, 1, LAYOUT, EPI, KCAT, false, 8>(a, s);
+}
+
 // 256 x 256 tiles (one workgroup per CU) for the leading c column-tiles and
 // 128 x 128 tiles (two per CU) for the rest, c chosen by plan_cost (8192 x
 // 3072 x 4096: 183 us with small tiles only, 197 us large only, 176 us with
@@ -555,10 +624,10 @@ static hipError_t pick(const GemmArgs &a, hipStream_t s) {
         best_c = c;
       }
     }
-    if (best_c >= tnb) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
+    if (best_c >= tnb) return run_big<LAYOUT, EPI, KCAT>(a, s);
     if (best_c > 0) {
       const int64_t c0 = best_c * 256;
-      const hipError_t e = run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(single_cols<LAYOUT, EPI>(a, 0, c0), s);
+      const hipError_t e = run_big<LAYOUT, EPI, KCAT>(single_cols<LAYOUT, EPI>(a, 0, c0), s);
       if (e != hipSuccess) return e;
       return run<128, 128, 2, 2, 2, 2, LAYOUT, EPI, KCAT>(single_cols<LAYOUT, EPI>(a, c0, a.N - c0), s);
     }
@@ -588,9 +657,10 @@ static GemmArgs dual_cols(const GemmArgs &a, int64_t c0, int64_t nc) {
 // too, half the work per tile).  The leading c column-tiles take the large
 // tiles and the rest the small ones, with c chosen to minimise the number
 // of rounds over the CUs, a large-tile round costing about 1.6 small-tile
-// rounds (measured on the SwiGLU shard: 8192 x 3584 x 4096 in 397 us with
-// large tiles only, 428 us with small ones, 375 us with 24 of the 28
-// column-tiles large, i.e. three whole rounds of them and one of small ones).
+// rounds (SwiGLU shard, 8192 x 3584 x 4096: 24 of the 28 column-tiles
+// large, i.e. three whole rounds of them, 309-323 us, and one round of
+// small ones, 72 us; with four waves per workgroup 397 us large tiles
+// only, 428 us small ones, 375 us split).
 template <int EPI>
 static hipError_t pick_dual(const GemmArgs &a, hipStream_t s) {
   const int64_t n = cus();
@@ -608,10 +678,10 @@ static hipError_t pick_dual(const GemmArgs &a, hipStream_t s) {
   }
   const int64_t c0 = std::min(best_c * 128, a.N);
   if (c0 > 0) {
-    const hipError_t e = run<256, 256, 2, 2, 2, 1, LAY_NN, EPI, false, true>(c0 < a.N ? dual_cols(a, 0, c0) : a, s);
+    const hipError_t e = run<256, 256, 2, 4, 2, 1, LAY_NN, EPI, false, true, 8>(c0 < a.N ? dual_cols(a, 0, c0) : a, s);
     if (e != hipSuccess || c0 == a.N) return e;
   }
-  return run<128, 256, 2, 2, 2, 1, LAY_NN, EPI, false, true>(c0 > 0 ? dual_cols(a, c0, a.N - c0) : a, s);
+  return run<128, 256, 2, 4, 2, 1, LAY_NN, EPI, false, true, 8>(c0 > 0 ? dual_cols(a, c0, a.N - c0) : a, s);
 }
 
 }  // namespace k64
