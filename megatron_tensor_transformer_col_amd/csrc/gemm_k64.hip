@@ -27,8 +27,6 @@
 //    side and keep both accumulators of an output element in one wave, so
 //    the gate and up values meet in registers: 256 x 128 output tiles carry
 //    the same per-slab traffic and MFMA work as a 256 x 256 single product.
-//    A K-concatenated B (NT) keeps four waves on its 256 x 256 tiles: its
-//    second set of DMA offsets does not fit two waves' registers per SIMD.
 //  * The compiler's register allocation is steered with the minimal-register
 //    scheduling strategy (build flag); the default one shuffled accumulators
 //    between AGPRs and VGPRs inside the loop.
@@ -590,12 +588,10 @@ static double plan_cost(int64_t big_tiles, int64_t small_tiles, int64_t n) {
   return big + 0.62 * small + (big_tiles > 0 && small_tiles > 0 ? 0.17 : 0.0);
 }
 
-// 256 x 256 tiles: eight waves in ping-pong; a K-concatenated B keeps four
-// (its second set of DMA offsets does not fit two waves' registers per SIMD)
+// 256 x 256 tiles: eight waves in ping-pong
 template <int LAYOUT, int EPI, bool KCAT>
 static hipError_t run_big(const GemmArgs &a, hipStream_t s) {
-  if constexpr (KCAT) return run<256, 256, 2, 2, 2, 1, LAYOUT, EPI, KCAT>(a, s);
-  else return run<256, 256, 2, 4, 2, 1, LAYOUT, EPI, KCAT, false, 8>(a, s);
+  return run<256, 256, 2, 4, 2, 1, LAYOUT, EPI, KCAT, false, 8>(a, s);
 }
 
 // 256 x 256 tiles (one workgroup per CU) for the leading c column-tiles and
