@@ -764,7 +764,7 @@ def cpu_baseline(synth, seconds):
                      "full_unsharded_gflop": round(flops_full / 1e9, 3),
                      "est_full_sec": round(sec * flops_full / flops_sample, 3), "sample": sample, "calls": calls}
 
-    # C1 tiny fp32 MLP, T 32, h 128, ffn 512: whole forward and backward, and the loop version
+    # tiny fp32 MLP, T 32, h 128, ffn 512: whole forward and backward, and the loop version
     w = synth.WORKLOADS["tiny_mlp_f32"]
     d = synth.make_mlp_inputs(w.tokens, w.h, w.ffn, "f32", seed=w.seed, with_dy=True)
     X, W1, W2, dY = d["X"].f64(), d["W1"].f64(), d["W2"].f64(), d["dY"].f64()
@@ -777,7 +777,7 @@ def cpu_baseline(synth, seconds):
     sec, n = _time(lambda: brute.mlp_gelu(Xl, W1l, W2l), 0.5)
     rec("tiny_mlp_f32_fwd_brute", sec, f1, f1, "whole workload, pure-Python loops, one core", n)
 
-    # C2 GPT-2-medium MLP forward on 1024-row blocks (the headline)
+    # GPT-2-medium MLP forward on 1024-row blocks (the headline)
     W = synth.WORKLOADS["gpt2m_mlp_bf16"]
     d = synth.make_mlp_inputs(W.tokens, W.h, W.ffn, "bf16", seed=W.seed)
     X, W1, W2 = d["X"].f64(), d["W1"].f64(), d["W2"].f64()
@@ -794,7 +794,7 @@ def cpu_baseline(synth, seconds):
     head = out["gpt2m_mlp_bf16_fwd"]
     del d, X, W1, W2
 
-    # C3 Llama SwiGLU MLP, forward and backward on 256 token rows, full weights
+    # Llama SwiGLU MLP, forward and backward on 256 token rows, full weights
     T3, h3, f3, r3 = 8192, 4096, 14336, 256
     X, Wg, Wu, Wd, dY = nrm((r3, h3), 1.0), nrm((h3, f3), 0.02), nrm((h3, f3), 0.02), nrm((f3, h3), 0.02), nrm((r3, h3), 1.0)
     g3 = 2.0 * h3 * f3
@@ -806,7 +806,7 @@ def cpu_baseline(synth, seconds):
         f"{rb} of {T3} token rows per call (dWg, dWu, dWd summed over those rows)", n)
     del X, Wg, Wu, Wd, dY
 
-    # C4 MHA, b 4 x s 2048, h 4096, 32 heads of 128, causal: one batch element
+    # MHA, b 4 x s 2048, h 4096, 32 heads of 128, causal: one batch element
     s4, h4, H4, b4 = 2048, 4096, 32, 4
     X = nrm((s4, h4), 1.0)
     Wq, Wk, Wv, Wo = (nrm((h4, h4), 0.02) for _ in range(4))
@@ -815,7 +815,7 @@ def cpu_baseline(synth, seconds):
     rec("mha_heads_bf16_fwd", sec, f4, b4 * f4, f"batch element 1 of {b4} (the oracle forms the full score matrix)", n)
     del X, Wq, Wk, Wv, Wo
 
-    # C5 decode MLP, 16 tokens, h 8192, ffn 28672: one shard's column block (3584) of W1 / row block of W2
+    # decode MLP, 16 tokens, h 8192, ffn 28672: one shard's column block (3584) of W1 / row block of W2
     h5, f5, n5 = 8192, 28672, 8
     x, W1, W2 = nrm((16, h5), 1.0), nrm((h5, f5 // n5), 0.02), nrm((f5 // n5, h5), 0.02)
     f5s = 2.0 * 2 * 16 * h5 * (f5 // n5)

@@ -28,7 +28,11 @@
 //    while the long ones finish).
 //  * K and V tiles move HBM -> LDS by direct DMA (global_load_lds_dwordx4,
 //    no staging registers) through two 4-deep rings of [key][d] tiles (K and
-//    V): each step consumes two blocks while the next two land.  Group 1
+//    V): each step consumes two blocks while the next two land.  Only the
+//    waves of group 1 issue the DMA, at the start of a step that begins with
+//    their exponentials, so the waves of group 0 start on the matrix cores
+//    without queueing behind the DMA instructions (all eight waves issuing:
+//    64 -> 59 us on a 4 x 2048-token, 8-head causal shard).  Group 1
 //    runs one block behind group 0 inside each step (softmax and P V of its
 //    previous block first, then the scores of its next one), so after every
 //    barrier one wave of each SIMD starts on the matrix cores and the other
@@ -59,8 +63,9 @@ static constexpr int FA_QW = 32;      // queries per wave
 static constexpr int FA_STAGES = 4;
 static constexpr int FA_TILE = FA_BKV * FA_D;  // elements of one K or V tile (16 KiB)
 static constexpr int FA_VRING = FA_STAGES * FA_TILE;  // element offset of the V ring (K ring first)
-static constexpr int FA_JN = 16 / FA_NW;       // wave-DMAs per wave per tile
-static constexpr int FA_ROWS_J = 4 * FA_NW;    // tile rows between one wave's DMA chunks
+static constexpr int FA_DW = FA_NW / 2;       // waves that issue the K/V DMA (group 1)
+static constexpr int FA_JN = 16 / FA_DW;       // wave-DMAs per issuing wave per tile
+static constexpr int FA_ROWS_J = 4 * FA_DW;    // tile rows between one wave's DMA chunks
 static constexpr float FA_RESCALE_LOG2 = 8.0f;
 static constexpr int64_t FA_MAX_LD = int64_t(1) << 24;  // keeps 64 rows' byte offsets in 32 bits
 
@@ -115,14 +120,14 @@ struct FaBlock {
     if (key0 + FA_BKV <= a.s) {
 #pragma unroll
       for (int j = 0; j < FA_JN; ++j)
-        dma16s(off, G + (int64_t)(key0 + FA_ROWS_J * j) * a.ldq, dst + (wave + FA_NW * j) * 1024);
+        dma16s(off, G + (int64_t)(key0 + FA_ROWS_J * j) * a.ldq, dst + (wq + FA_DW * j) * 1024);
     } else {
       const uint16_t *base = G + (int64_t)key0 * a.ldq;
       const uint32_t ldb = (uint32_t)a.ldq * 2u;
 #pragma unroll
       for (int j = 0; j < FA_JN; ++j) {
         const uint32_t r = (uint32_t)min(FA_ROWS_J * j + row_lo, a.s - 1 - key0);
-        dma16s(r * ldb + (off - (uint32_t)row_lo * ldb), base, dst + (wave + FA_NW * j) * 1024);
+        dma16s(r * ldb + (off - (uint32_t)row_lo * ldb), base, dst + (wq + FA_DW * j) * 1024);
       }
     }
   }
@@ -278,9 +283,11 @@ struct FaBlock {
     // V(2t-1), V(2t); in flight: K(2t+2), K(2t+3), V(2t+1), V(2t+2), each in
     // ring stage (block % 4) of its own ring.
     __syncthreads();  // the previous query block's readers are done with the rings
-    issue_k(a, Kg, 0, nkb);
-    issue_k(a, Kg, 1, nkb);
-    issue_v(a, Vg, 0, nkb);
+    if (grp == 1) {
+      issue_k(a, Kg, 0, nkb);
+      issue_k(a, Kg, 1, nkb);
+      issue_v(a, Vg, 0, nkb);
+    }
 
     // One code path for both groups (wave-uniform conditions only):
     // group 0 scores block 2t and finishes it in the same step, group 1
@@ -289,10 +296,12 @@ struct FaBlock {
     for (int t = 0; t <= nsteps; ++t) {
       wait_vmcnt<0>();   // this wave's DMAs for step t have landed
       __syncthreads();   // ... and every wave's; the stages used in step t-1 are free
-      issue_k(a, Kg, 2 * t + 2, nkb);
-      issue_k(a, Kg, 2 * t + 3, nkb);
-      issue_v(a, Vg, 2 * t + 1, nkb);
-      issue_v(a, Vg, 2 * t + 2, nkb);
+      if (grp == 1) {
+        issue_k(a, Kg, 2 * t + 2, nkb);
+        issue_k(a, Kg, 2 * t + 3, nkb);
+        issue_v(a, Vg, 2 * t + 1, nkb);
+        issue_v(a, Vg, 2 * t + 2, nkb);
+      }
       const int jp = 2 * t - grp;        // block finished in this step
       const int jn = 2 * t + grp;        // block scored in this step
       if (grp == 0 && jn < nkw) scores(jn % FA_STAGES, qf, st);
@@ -363,7 +372,7 @@ __global__ void __launch_bounds__(FA_NW * 64) flash_attn_kernel(FaArgs a) {
   fb.l16 = fb.lane & 15;
   // DMA slot of this lane: row 4*blk + lane/16, granule slot lane%16; rows
   // of one lane differ by multiples of 16, so the swizzles are per lane
-  fb.row_lo = 4 * fb.wave + (fb.lane >> 4);
+  fb.row_lo = 4 * fb.wq + (fb.lane >> 4);
   const uint32_t row_bytes = (uint32_t)fb.row_lo * (uint32_t)a.ldq * 2u;
   fb.koff = row_bytes + (uint32_t)(((fb.lane & 15) ^ (fb.row_lo & 15)) * 16);
   fb.voff = row_bytes + (uint32_t)(((fb.lane & 15) ^ ((fb.row_lo & 7) << 1)) * 16);
