@@ -20,7 +20,9 @@
 //    need ~360 VGPRs and measured 7% slower at one wave per SIMD), and keeps
 //    K, V (as MFMA B operands) and the fp32 dK^T, dV^T accumulators in
 //    registers while 64-query tiles of Q and dO, with the tile's lse2 and D
-//    rows, stream through LDS by direct DMA (two stages).  Per tile:
+//    rows, stream through LDS by direct DMA (two stages), issued by the
+//    second wave of each SIMD only, so the first starts on the matrix cores
+//    right after the barrier (all waves issuing: 2-3% slower).  Per tile:
 //    S = Q K^T and dP = dO V^T (Q / dO fragments by ds_read_b128), then
 //    P and dS in registers, then dV^T += dO^T P and dK^T += Q^T dS with the
 //    dO^T / Q^T operands from ds_read_b64_tr_b16 transpose reads.  The
@@ -183,8 +185,12 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(BwArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, l16 = lane & 15;
-  BwDma<NW> dma;
-  dma.init(wave, lane);
+  // the second wave of every SIMD (waves NW/2 ..) issues the tile DMA
+  constexpr int DW = NW / 2;
+  const bool dmaw = wave >= DW;
+  const int dwv = wave & (DW - 1);
+  BwDma<DW> dma;
+  dma.init(dwv, lane);
   const uint32_t lds0 = lds_addr(smem);
 
   int rank, bhs;
@@ -235,12 +241,14 @@ __global__ void __launch_bounds__(NW * 64) attn_bwd_dkdv_kernel(BwArgs a) {
     const float *Dr = a.Dr + ((int64_t)bi * a.hl + head) * a.s;
 
     // Tiles whose 64 rows all exist, with 16-byte aligned rows of lse2 / D
-    // (s % 4 == 0), also bring those rows into LDS (wave 0: lanes 0..15 lse2,
-    // 16..31 D, 32..63 the same again); other tiles read them from memory.
+    // (s % 4 == 0), also bring those rows into LDS (the first DMA wave: lanes
+    // 0..15 lse2, 16..31 D, 32..63 the same again); other tiles read them
+    // from memory.
     auto issue = [&](int jt, uint32_t dst) {
-      dma.tile(Qg, a.ldq, jt * BW_TROWS, a.s, dst, wave);
-      dma.tile(dOg, a.lddo, jt * BW_TROWS, a.s, dst + BW_TILE * 2, wave);
-      if (wave == 0 && jt * BW_TROWS + BW_TROWS <= a.s && (a.s & 3) == 0)
+      if (!dmaw) return;
+      dma.tile(Qg, a.ldq, jt * BW_TROWS, a.s, dst, dwv);
+      dma.tile(dOg, a.lddo, jt * BW_TROWS, a.s, dst + BW_TILE * 2, dwv);
+      if (dwv == 0 && jt * BW_TROWS + BW_TROWS <= a.s && (a.s & 3) == 0)
         dma16(reinterpret_cast<const uint16_t *>(((lane & 16) ? Dr : lse) + jt * BW_TROWS + 4 * (lane & 15)),
               dst + 4 * BW_TILE);
     };
