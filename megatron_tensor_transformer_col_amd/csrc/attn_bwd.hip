@@ -88,6 +88,7 @@ struct BwArgs {
 template <int NW>
 struct BwDma {
   static constexpr int JN = BW_TROWS / (4 * NW);  // wave-DMAs per wave per tile
+  static_assert((4 * NW) % 16 == 0 && JN >= 1, "a lane's rows must share their swizzle (16 apart)");
   int row_lo;
   uint32_t gran;  // byte offset of the fetched granule within its row
   __device__ __forceinline__ void init(int wave, int lane) {
