@@ -28,11 +28,14 @@
 //    while the long ones finish).
 //  * K and V tiles move HBM -> LDS by direct DMA (global_load_lds_dwordx4,
 //    no staging registers) through two 4-deep rings of [key][d] tiles (K and
-//    V): each step consumes two blocks while the next two land.  Only the
-//    waves of group 1 issue the DMA, at the start of a step that begins with
-//    their exponentials, so the waves of group 0 start on the matrix cores
-//    without queueing behind the DMA instructions (all eight waves issuing:
-//    64 -> 59 us on a 4 x 2048-token, 8-head causal shard).  Group 1
+//    V): each step consumes two blocks while the next two land.  The L2 ->
+//    LDS path takes a step's 64 KiB at ~44 B/cycle, and a wave cannot issue
+//    past a full DMA queue, so the issue blocks the issuing wave for ~1,500
+//    cycles.  Only the waves of group 0 issue it, right after their score
+//    MFMAs, while group 1 (one block behind) runs the exponentials and P V of
+//    its previous block: group 0's chain is the shorter one (4 x 2048-token,
+//    8-head causal shard: all eight waves issuing at the step start 64 us,
+//    group 1 at the step start 59, group 0 after its scores 57).  Group 1
 //    runs one block behind group 0 inside each step (softmax and P V of its
 //    previous block first, then the scores of its next one), so after every
 //    barrier one wave of each SIMD starts on the matrix cores and the other
@@ -63,7 +66,7 @@ static constexpr int FA_QW = 32;      // queries per wave
 static constexpr int FA_STAGES = 4;
 static constexpr int FA_TILE = FA_BKV * FA_D;  // elements of one K or V tile (16 KiB)
 static constexpr int FA_VRING = FA_STAGES * FA_TILE;  // element offset of the V ring (K ring first)
-static constexpr int FA_DW = FA_NW / 2;       // waves that issue the K/V DMA (group 1)
+static constexpr int FA_DW = FA_NW / 2;       // waves that issue the K/V DMA (group 0)
 static constexpr int FA_JN = 16 / FA_DW;       // wave-DMAs per issuing wave per tile
 static constexpr int FA_ROWS_J = 4 * FA_DW;    // tile rows between one wave's DMA chunks
 static constexpr float FA_RESCALE_LOG2 = 8.0f;
@@ -281,9 +284,10 @@ struct FaBlock {
     // after each barrier one wave of every SIMD starts on the matrix cores
     // and the other on the exponentials.  Resident in step t: K(2t), K(2t+1),
     // V(2t-1), V(2t); in flight: K(2t+2), K(2t+3), V(2t+1), V(2t+2), each in
-    // ring stage (block % 4) of its own ring.
+    // ring stage (block % 4) of its own ring, issued by group 0 after its
+    // scores (the stages they overwrite were last read in step t-1).
     __syncthreads();  // the previous query block's readers are done with the rings
-    if (grp == 1) {
+    if (grp == 0) {
       issue_k(a, Kg, 0, nkb);
       issue_k(a, Kg, 1, nkb);
       issue_v(a, Vg, 0, nkb);
@@ -296,15 +300,15 @@ struct FaBlock {
     for (int t = 0; t <= nsteps; ++t) {
       wait_vmcnt<0>();   // this wave's DMAs for step t have landed
       __syncthreads();   // ... and every wave's; the stages used in step t-1 are free
-      if (grp == 1) {
+      const int jp = 2 * t - grp;        // block finished in this step
+      const int jn = 2 * t + grp;        // block scored in this step
+      if (grp == 0 && jn < nkw) scores(jn % FA_STAGES, qf, st);
+      if (grp == 0) {
         issue_k(a, Kg, 2 * t + 2, nkb);
         issue_k(a, Kg, 2 * t + 3, nkb);
         issue_v(a, Vg, 2 * t + 1, nkb);
         issue_v(a, Vg, 2 * t + 2, nkb);
       }
-      const int jp = 2 * t - grp;        // block finished in this step
-      const int jn = 2 * t + grp;        // block scored in this step
-      if (grp == 0 && jn < nkw) scores(jn % FA_STAGES, qf, st);
       if (jp >= 0 && jp < nkw) {
         uint4 pf[2][2];
         softmax(jp, st, pf);
