@@ -49,7 +49,10 @@ def test_col_linear_identity_act_exact(dtype, M, K, N):
                                    # K % 64 == 0 and >= 64 tiles: the LDS-DMA kernel, ragged M / N
                                    (1000, 640, 1352), (3000, 1024, 2056), (8192, 64, 1024),
                                    # bf16: column-tiles split between 256 x 256 and 128 x 128 tiles
-                                   (3976, 256, 4104)])
+                                   (3976, 256, 4104),
+                                   # bf16, eight-wave 256 x 256 tiles with 2 and 3 slabs of K
+                                   # (the second ragged in M and N, split with 128 x 128 tiles)
+                                   (8192, 128, 4096), (3976, 192, 4104)])
 def test_row_partial_exact(dtype, M, K, N):
     note(f"row NN exact {dtype} {M}x{K}x{N}")
     rng = np.random.default_rng(7 * M + K)
