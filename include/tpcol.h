@@ -348,8 +348,10 @@ int tp_vocab_ce_total(int n, const float *const *shard_losses, float *total, voi
  *   dW2 [Ni x K], db1 [Ni] (optional; GELU only), dXi [M x K] ldd x.
  *   ws: tp_mlp_shard_backward_workspace() bytes; holds dH_i, H_i and dZ_i
  *   ([M x Ni] each, dtype; dZg and dZu for SwiGLU) and, without SwiGLU, a
- *   second dH-sized region and up to 64 fp32 rows [64 x Ni] of partial
- *   column sums for db1.  After the recompute the dH region (GELU: with the
+ *   second dH-sized region and max(64, ceil(M / 128)) fp32 rows [. x Ni]
+ *   of partial column sums for db1 (per 128-row tile of dZ when the
+ *   recompute's epilogue forms them, else per row split of a column-sum
+ *   pass).  After the recompute the dH region (GELU: with the
  *   region after it) holds fp32 K-range partials of the weight gradients.
  *   Every partial is added in a fixed order, so all outputs are
  *   deterministic.

@@ -137,7 +137,7 @@ BwdWs bwd_ws(int dtype, int act, int64_t M, int64_t Ni) {
   w.H = act == TP_ACT_SWIGLU ? one : 2 * one;
   w.dZ = w.H + one;
   w.cs = w.dZ + (act == TP_ACT_SWIGLU ? round256((size_t)M * 2 * (size_t)Ni * e) : one);
-  w.total = w.cs + (act == TP_ACT_SWIGLU ? 0 : round256(colsum_workspace(Ni)));
+  w.total = w.cs + (act == TP_ACT_SWIGLU ? 0 : round256(colsum_workspace(M, Ni)));
   return w;
 }
 
@@ -740,6 +740,7 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
   // split-K partials of the weight-gradient GEMMs
   float *dHpart = M > 0 ? reinterpret_cast<float *>(base + L.dH) : nullptr;
   const size_t dHpart_bytes = M > 0 ? L.H - L.dH : 0;
+  int db1_tiles = 0;  // row-tiles of db1 partials the recompute's epilogue wrote
 
   if (M > 0) {
     // dH = dY W2^T  (row-parallel layer, input gradient of this shard's slice)
@@ -767,6 +768,12 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
     } else {
       r.epi = EPI_GELU_BWD;
       r.bias = b1;
+      // db1's per-row-tile partials straight from the epilogue, if the
+      // kernel that takes the product can (else the column-sum kernels)
+      if (db1 != nullptr) {
+        r.colsum = reinterpret_cast<float *>(base + L.cs);
+        r.colsum_tiles = &db1_tiles;
+      }
     }
     TRY(hip_status(launch_gemm(r, s), "recompute GEMM"));
   }
@@ -800,7 +807,10 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
   }
   if (db1 != nullptr) {
     float *cs = M > 0 ? reinterpret_cast<float *>(base + L.cs) : nullptr;  // M == 0: db1 = 0
-    TRY(hip_status(launch_colsum(dtype, M, Ni, dZ, ldz, db1, cs, s), "db1"));
+    if (db1_tiles > 0)
+      TRY(hip_status(launch_colsum_final(db1_tiles, Ni, cs, db1, s), "db1"));
+    else
+      TRY(hip_status(launch_colsum(dtype, M, Ni, dZ, ldz, db1, cs, s), "db1"));
   }
 
   if (M > 0) {

@@ -261,6 +261,7 @@ template <typename T, int BM, int BN, int BK, int WGM, int WGN, int LAYOUT, int 
           bool KCAT>
 static hipError_t run_gemm(const GemmArgs &a, hipStream_t s) {
   GemmParams p;
+  p.colsum = nullptr;  // only the 64-deep kernel writes column sums
   p.A = a.A; p.lda = a.lda;
   p.B = a.B; p.ldb = a.ldb;
   p.B2 = a.B2; p.ldb2 = a.ldb2;

@@ -23,6 +23,9 @@ struct GemmParams {
   // grouped TN split-K: grid rows [zsplit, 2 zsplit) compute A2^T B2
   const void *A2; int64_t lda2;
   int zsplit;
+  // GELU-backward epilogue: per row-tile column sums of C ([tiles_m][N]
+  // fp32, the bf16 values as stored), or NULL
+  float *colsum;
 };
 
 template <typename T>

@@ -201,7 +201,11 @@ gemm_k64_kernel(GemmParams pin) {
   static_assert(!BWD || STAGED3, "the backward epilogues are staged");
   static_assert(DUAL == (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_BWD), "SwiGLU epilogues need both products");
   constexpr int RING_B = STAGES * STAGE * 2;
-  constexpr int STG_B = STAGED ? BM * SROW : (STAGED3 ? 2 * BM * SR3 : 0);
+  // GELU backward on 128 x 128 tiles of four waves: the per-row-tile column
+  // sums of dZ (db1) reduce through a [16][BNO] fp32 area after the staging
+  constexpr bool CSUM = EPI == EPI_GELU_BWD && BM == 128 && BNO == 128 && NWV == 4;
+  constexpr int CSUM_B = CSUM ? 16 * BNO * 4 : 0;
+  constexpr int STG_B = STAGED ? BM * SROW : (STAGED3 ? 2 * BM * SR3 + CSUM_B : 0);
   static_assert(RING_B <= LDS_CAP && STG_B <= LDS_CAP, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[RING_B > STG_B ? RING_B : STG_B];
 
@@ -447,6 +451,7 @@ gemm_k64_kernel(GemmParams pin) {
     constexpr int NOUT = EPI == EPI_SWIGLU_BWD ? 3 : 2;
     char *dhs = smem;
     char *out = smem + BM * SR3;
+    float *red = reinterpret_cast<float *>(smem + 2 * BM * SR3);  // [16][BNO] (CSUM)
     if (p.bias != nullptr) {
 #pragma unroll
       for (int j = 0; j < TNO; ++j) {
@@ -495,6 +500,40 @@ gemm_k64_kernel(GemmParams pin) {
         }
       }
       __syncthreads();
+      if constexpr (CSUM) {
+        // db1's share of this tile: thread (row group rg, 8-column chunk
+        // cc) adds the stored dZ values of rows rg, rg + 16, ... in order;
+        // the 16 row groups are added after the barrier that ends this output
+        if (which == 0 && p.colsum != nullptr) {
+          const int cc = threadIdx.x & 15, rg = threadIdx.x >> 4;
+          const int rows = min(BM, M - m0);
+          float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < BM / 16; ++k) {
+            const int rl = rg + 16 * k;
+            if (rl < rows) {
+              const uint4 v = *reinterpret_cast<const uint4 *>(out + rl * SR3 + cc * 16);
+              const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                cs[2 * q] += bf2f((uint16_t)(w[q] & 0xffffu));
+                cs[2 * q + 1] += bf2f((uint16_t)(w[q] >> 16));
+              }
+            }
+          }
+          *reinterpret_cast<f32x4_t *>(red + rg * BNO + cc * 8) = (f32x4_t){cs[0], cs[1], cs[2], cs[3]};
+          *reinterpret_cast<f32x4_t *>(red + rg * BNO + cc * 8 + 4) = (f32x4_t){cs[4], cs[5], cs[6], cs[7]};
+        }
+        if (which == 1 && p.colsum != nullptr && (int)threadIdx.x < BNO) {
+          const int col = n0 + (int)threadIdx.x;
+          if (col < N) {
+            float t = red[threadIdx.x];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) t += red[r * BNO + threadIdx.x];
+            p.colsum[(int64_t)tm * N + col] = t;
+          }
+        }
+      }
       // dZ (dZg) -> C, H -> C2, dZu -> C3
       void *C = which == 0 ? p.C : (which == 1 ? p.C2 : p.C3);
       const int64_t ldc = which == 0 ? p.ldc : (which == 1 ? p.ldc2 : p.ldc3);
@@ -544,6 +583,13 @@ static hipError_t run(const GemmArgs &a, hipStream_t s) {
   p.zstride = a.zstride;
   p.A2 = a.A2; p.lda2 = a.lda2;
   p.zsplit = a.splits;
+  p.colsum = nullptr;
+  if constexpr (EPI == EPI_GELU_BWD && BM == 128 && BNO == 128 && NWV == 4) {
+    if (a.colsum != nullptr && a.splits * a.groups == 1) {
+      p.colsum = a.colsum;
+      if (a.colsum_tiles != nullptr) *a.colsum_tiles = p.tiles_m;
+    }
+  }
   hipLaunchKernelGGL((gemm_k64_kernel<BM, BN, WGM, WGN, STAGES, OCC, LAYOUT, EPI, KCAT, DUAL, NWV>),
                      dim3((unsigned)(p.tiles_m * p.tiles_n), (unsigned)(a.splits * a.groups)), dim3(NWV * 64), 0, s,
                      p);

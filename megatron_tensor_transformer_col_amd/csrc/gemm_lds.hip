@@ -494,6 +494,7 @@ template <int BM, int BN, int LBK, int WGM, int WGN, int LAYOUT, int EPI, bool D
           int STAGES, bool PREFETCH>
 static hipError_t run_lds(const GemmArgs &a, hipStream_t s) {
   GemmParams p;
+  p.colsum = nullptr;  // only the 64-deep kernel writes column sums
   p.A = a.A; p.lda = a.lda;
   p.B = a.B; p.ldb = a.ldb;
   p.B2 = a.B2; p.ldb2 = a.ldb2;

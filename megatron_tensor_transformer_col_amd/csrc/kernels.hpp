@@ -51,6 +51,12 @@ struct GemmArgs {
   // shape, A2 . B2 (B2 / ldb2 above), whose partials follow the first's
   const void *A2 = nullptr; int64_t lda2 = 0;
   int groups = 1;
+  // EPI_GELU_BWD: where the kernel may also write the column sums of C per
+  // row-tile ([row-tiles][N] fp32, rows added in order; colsum_rows() of
+  // them at most); if it does, it stores the row-tile count in
+  // *colsum_tiles (a host int), otherwise leaves it untouched
+  float *colsum = nullptr;
+  int *colsum_tiles = nullptr;
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
@@ -129,8 +135,13 @@ hipError_t launch_vocab_loss(int dtype, int64_t T, int64_t Vi, int64_t v0, const
                              const int32_t *targets, const float *lse, float *row_loss, float *shard_loss,
                              hipStream_t s);
 hipError_t launch_vocab_total(int n, const float *const *losses, float *total, hipStream_t s);
-size_t colsum_workspace(int64_t N);  // fp32 partial bytes launch_colsum needs
+// fp32 partial bytes launch_colsum needs for M x N, and which a GEMM's
+// column-sum output of M rows fits
+size_t colsum_workspace(int64_t M, int64_t N);
+int64_t colsum_rows(int64_t M);  // rows of partials that workspace holds
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,
                          float *part, hipStream_t s);
+// db[n] = sum over rows r < rows of part[r][n], in row order
+hipError_t launch_colsum_final(int rows, int64_t N, const float *part, float *db, hipStream_t s);
 
 }  // namespace tpcol

@@ -110,7 +110,15 @@ static int colsum_splits(int64_t M) {
   return (int)(s < 1 ? 1 : (s > CS_MAX_SPLITS ? CS_MAX_SPLITS : s));
 }
 
-size_t colsum_workspace(int64_t N) { return (size_t)CS_MAX_SPLITS * (size_t)(N > 0 ? N : 0) * sizeof(float); }
+// room for the 64 row splits of colsum_partial_kernel or one row per 128
+// rows of M (a GEMM epilogue's per-row-tile sums), whichever is more
+int64_t colsum_rows(int64_t M) {
+  const int64_t tiles = (M + 127) / 128;
+  return tiles > CS_MAX_SPLITS ? tiles : CS_MAX_SPLITS;
+}
+size_t colsum_workspace(int64_t M, int64_t N) {
+  return (size_t)colsum_rows(M) * (size_t)(N > 0 ? N : 0) * sizeof(float);
+}
 
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -178,6 +186,13 @@ colsum_final_kernel(int splits, int64_t N, const float *__restrict__ part, float
       if (y0 + j < splits) t += v[j];
   }
   db[c] = t;
+}
+
+hipError_t launch_colsum_final(int rows, int64_t N, const float *part, float *db, hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  if (rows < 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, rows, N, part, db);
+  return hipGetLastError();
 }
 
 hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_t ldz, float *db,

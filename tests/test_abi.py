@@ -94,6 +94,8 @@ def test_workspace_sizes():
     assert tp.tp_mlp_shard_backward_workspace(1, 1, 8192, 1024) == 4 * 8192 * 1024 * 2 + 64 * 1024 * 4
     assert tp.tp_mlp_shard_backward_workspace(1, 2, 8192, 3584) == 4 * 8192 * 3584 * 2
     assert tp.tp_mlp_shard_backward_workspace(0, 1, 32, 256) == 4 * 32 * 256 * 4 + 64 * 256 * 4
+    # db1 partials: one row per 128-row tile of dZ once that exceeds 64 rows
+    assert tp.tp_mlp_shard_backward_workspace(1, 1, 16384, 1024) == 4 * 16384 * 1024 * 2 + 128 * 1024 * 4
     # large-M linear calls need no workspace; the decode path needs split-K partials
     assert tp.tp_col_linear_gelu_workspace(1, 1, 8192, 1024, 1024) == 0
     assert tp.tp_col_linear_gelu_workspace(1, 1, 16, 8192, 3584) > 0
