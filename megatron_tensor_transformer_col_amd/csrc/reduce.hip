@@ -101,7 +101,8 @@ hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const fl
 // vectors x 8 row lanes over the rows of split y; a thread adds rows
 // lane, lane + 8, ... of its vector in row order (4 loads in flight), the 8
 // lanes are added in lane order through LDS, and the sums go to part[y][c].
-// Pass 2: db[c] = sum over y of part[y][c] in split order.
+// Pass 2 (colsum_final_kernel): db[c] = sum over y of part[y][c] in a fixed
+// order (see the kernel).
 static constexpr int CS_MAX_SPLITS = 64;
 static constexpr int CS_MIN_ROWS = 64;  // rows per split at least
 
@@ -172,26 +173,42 @@ colsum_partial_kernel(int64_t M, int64_t N, const T *__restrict__ dZ, int64_t ld
   }
 }
 
+// db[c] = sum over rows y < splits of part[y][c]: 16 lanes of a wave per
+// column, lane l adding rows l, l + 16, ... in order, then the 16 lane
+// sums added in lane order (a fixed order; one round trip of loads per
+// 16 rows instead of a chain over all of them)
 __global__ void __launch_bounds__(256)
 colsum_final_kernel(int splits, int64_t N, const float *__restrict__ part, float *__restrict__ db) {
-  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (c >= N) return;
+  const int lane = threadIdx.x & 63, l = lane & 15;
+  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // 16 columns per wave
   float t = 0.f;
-  for (int y0 = 0; y0 < splits; y0 += 8) {
-    float v[8];
+  if (c < N) {
+    for (int y0 = 0; y0 < splits; y0 += 64) {
+      float v[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = y0 + j < splits ? part[(int64_t)(y0 + j) * N + c] : 0.f;
+      for (int j = 0; j < 4; ++j) {
+        const int y = y0 + 16 * j + l;
+        v[j] = y < splits ? part[(int64_t)y * N + c] : 0.f;
+      }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (y0 + j < splits) t += v[j];
+      for (int j = 0; j < 4; ++j)
+        if (y0 + 16 * j + l < splits) t += v[j];
+    }
   }
-  db[c] = t;
+  // lane sums in lane order: lane 0 of each 16-lane group collects 1..15
+  float tot = t;
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    const float o = __shfl(t, (lane & ~15) + k);
+    if (l == 0) tot += o;
+  }
+  if (l == 0 && c < N) db[c] = tot;
 }
 
 hipError_t launch_colsum_final(int rows, int64_t N, const float *part, float *db, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   if (rows < 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, rows, N, part, db);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N * 16 + 255) / 256)), dim3(256), 0, s, rows, N, part, db);
   return hipGetLastError();
 }
 
@@ -214,7 +231,7 @@ hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, splits, N,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N * 16 + 255) / 256)), dim3(256), 0, s, splits, N,
                      part, db);
   return hipGetLastError();
 }
