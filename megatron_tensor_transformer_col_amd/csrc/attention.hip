@@ -134,13 +134,13 @@ struct FaBlock {
       }
     }
   }
-  // Block kb goes to ring stage kb % 4; a block index past the last block
-  // (nkb - 1) fetches the last block again into that stage, which nobody reads.
+  // Block kb goes to ring stage kb % 4; block indexes past the last block
+  // (nkb - 1) fetch nothing (every wait is for all of a wave's DMAs).
   __device__ __forceinline__ void issue_k(const FaArgs &a, const uint16_t *Kg, int kb, int nkb) const {
-    issue_tile(a, Kg, koff, min(kb, nkb - 1), lds0 + (uint32_t)((kb % FA_STAGES) * FA_TILE * 2));
+    if (kb < nkb) issue_tile(a, Kg, koff, kb, lds0 + (uint32_t)((kb % FA_STAGES) * FA_TILE * 2));
   }
   __device__ __forceinline__ void issue_v(const FaArgs &a, const uint16_t *Vg, int kb, int nkb) const {
-    issue_tile(a, Vg, voff, min(kb, nkb - 1), lds0 + (uint32_t)((FA_VRING + (kb % FA_STAGES) * FA_TILE) * 2));
+    if (kb < nkb) issue_tile(a, Vg, voff, kb, lds0 + (uint32_t)((FA_VRING + (kb % FA_STAGES) * FA_TILE) * 2));
   }
 
   // S^T[key][q] for the 64 keys of a stage x the wave's 32 queries
@@ -316,7 +316,7 @@ struct FaBlock {
       }
       if (grp == 1 && jn < nkw) scores(jn % FA_STAGES, qf, st);
     }
-    wait_vmcnt<0>();  // the trailing re-issued blocks land before the ring is reused
+    wait_vmcnt<0>();
     __syncthreads();  // every wave is done reading the ring
 
     // ---- merge the two groups' states through LDS (the ring is free now):
