@@ -68,6 +68,34 @@ __device__ __forceinline__ void store16_wt(void *dst, const void *lds_src) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(dst), "v"(v) : "memory");
 }
 
+// Bias of a lane's TF column groups (columns col0 + 16 f .. +3, zero from N
+// on; N is a multiple of 4): all loads are issued before the first wait (a
+// column past N reads column 0, so no load depends on a branch).
+template <typename BT, int TF>
+__device__ __forceinline__ void load_bias(const BT *bias, int col0, int N, float (&bv)[TF][4]) {
+  using Raw = typename std::conditional<sizeof(BT) == 2, uint2, float4>::type;
+  Raw raw[TF];
+#pragma unroll
+  for (int f = 0; f < TF; ++f) {
+    const int col = col0 + 16 * f;
+    raw[f] = *reinterpret_cast<const Raw *>(bias + (col < N ? col : 0));
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int f = 0; f < TF; ++f) {
+    const bool ok = col0 + 16 * f < N;
+    float v[4];
+    if constexpr (sizeof(BT) == 2) {
+      v[0] = bf2f((uint16_t)(raw[f].x & 0xffffu)); v[1] = bf2f((uint16_t)(raw[f].x >> 16));
+      v[2] = bf2f((uint16_t)(raw[f].y & 0xffffu)); v[3] = bf2f((uint16_t)(raw[f].y >> 16));
+    } else {
+      v[0] = raw[f].x; v[1] = raw[f].y; v[2] = raw[f].z; v[3] = raw[f].w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) bv[f][r] = ok ? v[r] : 0.f;
+  }
+}
+
 // k-contiguous 128-byte rows: slot of granule c in row r is c ^ swz_k(r)
 __device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
 // m/n-contiguous rows: granule index bits 1..3 XOR-ed with row bits
@@ -443,68 +471,74 @@ gemm_k64_kernel(GemmParams pin) {
   }
   if constexpr (STAGED3) {
     // activation backward: dH comes into LDS by coalesced 16-byte loads,
-    // then each output (GELU: dZ, H; SwiGLU: dZg, H, dZu) is computed from
-    // the accumulators and dH one tile at a time, written to LDS and stored
-    // as whole row chunks (reading dH element by element between stores
-    // would wait on every store before it)
+    // then the outputs (GELU: dZ, H; SwiGLU: dZg, H, dZu) are computed from
+    // the accumulators and dH, written to LDS and stored as whole row
+    // chunks (reading dH element by element between stores would wait on
+    // every store before it): GELU's two in one pass (dZ to a second tile,
+    // H over dH), SwiGLU's three one tile at a time
     constexpr int CPR = BNO * 2 / 16;
     constexpr int NOUT = EPI == EPI_SWIGLU_BWD ? 3 : 2;
+    constexpr int DHN = (BM * CPR + NWV * 64 - 1) / (NWV * 64);  // dH chunks per thread
     char *dhs = smem;
     char *out = smem + BM * SR3;
     float *red = reinterpret_cast<float *>(smem + 2 * BM * SR3);  // [16][BNO] (CSUM)
-    if (p.bias != nullptr) {
+    // every dH load of the thread is in flight before the first one is
+    // waited on (one memory latency per tile, not one per chunk)
+    uint4 dhv[DHN];
 #pragma unroll
-      for (int j = 0; j < TNO; ++j) {
-        const int col = n0 + wn * WTNO + j * 16 + g * 4;
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (col < N) load4(static_cast<const uint16_t *>(p.bias) + col, bv);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] += bv[r];
-      }
-    }
-    __syncthreads();  // every wave is done reading the ring
-    for (int c = threadIdx.x; c < BM * CPR; c += NWV * 64) {
+    for (int k = 0; k < DHN; ++k) {
+      const int c = (int)threadIdx.x + k * NWV * 64;
       const int rl = c / CPR, cc = c % CPR;
       const int row = m0 + rl, col = n0 + cc * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (row < M && col < N)
-        v = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
-      *reinterpret_cast<uint4 *>(dhs + rl * SR3 + cc * 16) = v;
+      dhv[k] = make_uint4(0u, 0u, 0u, 0u);
+      if (c < BM * CPR && row < M && col < N)
+        dhv[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
+    }
+    if (p.bias != nullptr) {
+      float bv[TNO][4];
+      load_bias(static_cast<const uint16_t *>(p.bias), n0 + wn * WTNO + g * 4, N, bv);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TNO; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] += bv[j][r];
+    }
+    __syncthreads();  // every wave is done reading the ring
+#pragma unroll
+    for (int k = 0; k < DHN; ++k) {
+      const int c = (int)threadIdx.x + k * NWV * 64;
+      if (c < BM * CPR) *reinterpret_cast<uint4 *>(dhs + (c / CPR) * SR3 + (c % CPR) * 16) = dhv[k];
     }
     __syncthreads();
-#pragma unroll
-    for (int which = 0; which < NOUT; ++which) {
+    if constexpr (EPI == EPI_GELU_BWD) {
+      // one pass: Phi(z) and phi(z) come from a single erf evaluation and
+      // give both dZ = dH (Phi + z phi) (to `out`) and H = z Phi (over its
+      // own dH, which this lane alone reads)
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
 #pragma unroll
         for (int j = 0; j < TNO; ++j) {
           const int off = (wm * WTM + i * 16 + l16) * SR3 + (wn * WTNO + j * 16 + g * 4) * 2;
-          float dh[4], o[4];
+          float dh[4], dz[4], h[4];
           load4(reinterpret_cast<const uint16_t *>(dhs + off), dh);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float z = acc[i][j][r];
-            if constexpr (EPI == EPI_GELU_BWD) {
-              o[r] = which == 0 ? dh[r] * gelu_grad_f(z) : gelu_f(z);
-            } else {
-              // z = gate pre-activation, u = up projection
-              const float u = acc[i][DUAL ? TNO + j : j][r];
-              const float sg = sigmoid_f(z);
-              const float sl = z * sg;
-              o[r] = which == 0 ? dh[r] * u * (sg * (1.0f + z * (1.0f - sg))) : (which == 1 ? sl * u : dh[r] * sl);
-            }
+            const PhiResult f = normal_cdf_pdf(z);
+            dz[r] = dh[r] * fmaf(z, f.pdf, f.phi_cdf);
+            h[r] = z * f.phi_cdf;
           }
-          store4(reinterpret_cast<uint16_t *>(out + off), o);
+          store4(reinterpret_cast<uint16_t *>(out + off), dz);
+          store4(reinterpret_cast<uint16_t *>(dhs + off), h);
         }
       }
       __syncthreads();
       if constexpr (CSUM) {
         // db1's share of this tile: thread (row group rg, 8-column chunk
-        // cc) adds the stored dZ values of rows rg, rg + 16, ... in order;
-        // the 16 row groups are added after the barrier that ends this output
-        if (which == 0 && p.colsum != nullptr) {
+        // cc) adds the stored dZ values of rows rg, rg + 16, ... in order,
+        // then (after a barrier) the 16 row groups are added in order
+        if (p.colsum != nullptr) {
           const int cc = threadIdx.x & 15, rg = threadIdx.x >> 4;
           const int rows = min(BM, M - m0);
           float cs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -524,17 +558,55 @@ gemm_k64_kernel(GemmParams pin) {
           *reinterpret_cast<f32x4_t *>(red + rg * BNO + cc * 8) = (f32x4_t){cs[0], cs[1], cs[2], cs[3]};
           *reinterpret_cast<f32x4_t *>(red + rg * BNO + cc * 8 + 4) = (f32x4_t){cs[4], cs[5], cs[6], cs[7]};
         }
-        if (which == 1 && p.colsum != nullptr && (int)threadIdx.x < BNO) {
-          const int col = n0 + (int)threadIdx.x;
-          if (col < N) {
-            float t = red[threadIdx.x];
+      }
+      // dZ -> C, H -> C2
+      for (int c = threadIdx.x; c < BM * CPR; c += NWV * 64) {
+        const int rl = c / CPR, cc = c % CPR;
+        const int row = m0 + rl, col = n0 + cc * 8;
+        if (row < M && col < N) {
+          store16_wt(static_cast<uint16_t *>(p.C) + (int64_t)row * p.ldc + col, out + rl * SR3 + cc * 16);
+          store16_wt(static_cast<uint16_t *>(p.C2) + (int64_t)row * p.ldc2 + col, dhs + rl * SR3 + cc * 16);
+        }
+      }
+      if constexpr (CSUM) {
+        if (p.colsum != nullptr) {
+          __syncthreads();
+          if ((int)threadIdx.x < BNO) {
+            const int col = n0 + (int)threadIdx.x;
+            if (col < N) {
+              float t = red[threadIdx.x];
 #pragma unroll
-            for (int r = 1; r < 16; ++r) t += red[r * BNO + threadIdx.x];
-            p.colsum[(int64_t)tm * N + col] = t;
+              for (int r = 1; r < 16; ++r) t += red[r * BNO + threadIdx.x];
+              p.colsum[(int64_t)tm * N + col] = t;
+            }
           }
         }
       }
-      // dZ (dZg) -> C, H -> C2, dZu -> C3
+    } else {
+    // SwiGLU: the three outputs one after the other through `out`
+#pragma unroll
+    for (int which = 0; which < NOUT; ++which) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TNO; ++j) {
+          const int off = (wm * WTM + i * 16 + l16) * SR3 + (wn * WTNO + j * 16 + g * 4) * 2;
+          float dh[4], o[4];
+          load4(reinterpret_cast<const uint16_t *>(dhs + off), dh);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // z = gate pre-activation, u = up projection
+            const float z = acc[i][j][r];
+            const float u = acc[i][DUAL ? TNO + j : j][r];
+            const float sg = sigmoid_f(z);
+            const float sl = z * sg;
+            o[r] = which == 0 ? dh[r] * u * (sg * (1.0f + z * (1.0f - sg))) : (which == 1 ? sl * u : dh[r] * sl);
+          }
+          store4(reinterpret_cast<uint16_t *>(out + off), o);
+        }
+      }
+      __syncthreads();
+      // dZg -> C, H -> C2, dZu -> C3
       void *C = which == 0 ? p.C : (which == 1 ? p.C2 : p.C3);
       const int64_t ldc = which == 0 ? p.ldc : (which == 1 ? p.ldc2 : p.ldc3);
       for (int c = threadIdx.x; c < BM * CPR; c += NWV * 64) {
@@ -544,6 +616,7 @@ gemm_k64_kernel(GemmParams pin) {
           store16_wt(static_cast<uint16_t *>(C) + (int64_t)row * ldc + col, out + rl * SR3 + cc * 16);
       }
       __syncthreads();
+    }
     }
     return;
   }
