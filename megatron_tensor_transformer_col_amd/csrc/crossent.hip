@@ -145,25 +145,36 @@ vocab_loss_kernel(const T *__restrict__ Z, int64_t ldz, int64_t T_, int64_t Vi, 
   __shared__ float part[CE_LT];
   float acc = 0.f;
   for (int64_t r0 = threadIdx.x; r0 < T_; r0 += (int64_t)CE_LT * CE_LB) {
+    // targets and lse of rows past T_ read row T_ - 1 (unused); the logit
+    // gathers run only for this shard's targets, and nothing reads a
+    // gathered value before every gather of the round is issued
     int64_t c[CE_LB];
 #pragma unroll
     for (int u = 0; u < CE_LB; ++u) {
       const int64_t t = r0 + (int64_t)u * CE_LT;
-      c[u] = t < T_ ? (int64_t)targets[t] - v0 : -1;
+      c[u] = (int64_t)targets[t < T_ ? t : T_ - 1] - v0;
     }
-    float z[CE_LB], l[CE_LB];
+    bool mine[CE_LB];
+    uint32_t zr[CE_LB];  // raw bits, each in its own 32-bit register
+    float l[CE_LB];
 #pragma unroll
     for (int u = 0; u < CE_LB; ++u) {
       const int64_t t = r0 + (int64_t)u * CE_LT;
-      const bool mine = c[u] >= 0 && c[u] < Vi;
-      z[u] = mine ? (float)Elem<T>::to_f(Z[t * ldz + c[u]]) : 0.f;
-      l[u] = mine ? lse[t] : 0.f;
+      const int64_t tc = t < T_ ? t : T_ - 1;
+      mine[u] = t < T_ && c[u] >= 0 && c[u] < Vi;
+      zr[u] = 0u;
+      if (mine[u]) {
+        if constexpr (sizeof(T) == 2) zr[u] = (uint32_t)Z[tc * ldz + c[u]];  // widened only after every gather
+        else zr[u] = __float_as_uint(Z[tc * ldz + c[u]]);
+      }
+      l[u] = lse[tc];
     }
 #pragma unroll
     for (int u = 0; u < CE_LB; ++u) {
       const int64_t t = r0 + (int64_t)u * CE_LT;
       if (t >= T_) break;
-      const float v = (c[u] >= 0 && c[u] < Vi) ? l[u] - z[u] : 0.f;
+      const float zf = __uint_as_float(sizeof(T) == 2 ? zr[u] << 16 : zr[u]);
+      const float v = mine[u] ? l[u] - zf : 0.f;
       acc += v;
       if (row_loss != nullptr) row_loss[t] = v;
     }
