@@ -601,39 +601,39 @@ def run_op(torch, tp, synth, name, iters):
         src = torch.empty(256 << 20, dtype=torch.float32, device="cuda:0").fill_(1.0)
         dst = torch.empty_like(src)
         fn = lambda: dst.copy_(src)
-    elif name.startswith("c2_") and name != "c2_sum_cold":
+    elif name in ("gpt2m_col", "gpt2m_row", "gpt2m_sum", "gpt2m_step"):
         hl = Headline(torch, tp, synth)
-        fn = {"c2_col": lambda: hl.col(0), "c2_row": lambda: hl.row(0), "c2_sum": hl.total,
-              "c2_step": lambda: hl.step(None)}[name]
+        fn = {"gpt2m_col": lambda: hl.col(0), "gpt2m_row": lambda: hl.row(0), "gpt2m_sum": hl.total,
+              "gpt2m_step": lambda: hl.step(None)}[name]
     else:
         R = Rows(torch, tp)
-        if name.startswith("c3_"):
+        if name in ("llama_swiglu_col", "llama_down", "llama_swiglu_bwd"):
             s = R.swiglu()
-            fn = {"c3_col": lambda: R.swiglu_col(s), "c3_down": lambda: R.swiglu_down(s),
-                  "c3_bwd": lambda: R.swiglu_bwd(s)}[name]
-        elif name == "c11_mlp_bwd":
+            fn = {"llama_swiglu_col": lambda: R.swiglu_col(s), "llama_down": lambda: R.swiglu_down(s),
+                  "llama_swiglu_bwd": lambda: R.swiglu_bwd(s)}[name]
+        elif name == "gpt2m_mlp_bwd":
             s = R.gelu_mlp()
             fn = lambda: R.gelu_mlp_bwd(s)
-        elif name == "c4_attn":
+        elif name == "mha_shard":
             s = R.mha()
             fn = lambda: R.attn(s)
-        elif name == "c6_gqa":
+        elif name == "gqa_shard":
             s = R.gqa()
             fn = lambda: R.gqa_attn(s)
-        elif name in ("c9_attn_bwd", "c10_gqa_bwd"):
-            s = R.mha_bwd(None if name == "c9_attn_bwd" else 2)
+        elif name in ("mha_shard_bwd", "gqa_shard_bwd"):
+            s = R.mha_bwd(None if name == "mha_shard_bwd" else 2)
             fn = lambda: R.attn_bwd(s)
-        elif name == "c7_spln":
+        elif name == "sp_layernorm":
             s = R.sp_ln()
             fn = lambda: R.sp_ln_step(s)
-        elif name == "c7_spln_cold":
+        elif name == "sp_layernorm_cold":
             sl = [R.sp_ln() for _ in range(3)]
             it = [0]
 
             def fn():
                 R.sp_ln_step(sl[it[0] % 3])
                 it[0] += 1
-        elif name == "c2_sum_cold":
+        elif name == "gpt2m_sum_cold":
             sets = [{"P": [R.empty((8192, 1024), torch.float32).normal_() for _ in range(4)],
                      "Y": R.empty((8192, 1024), torch.float32)} for _ in range(3)]
             it = [0]
@@ -642,12 +642,12 @@ def run_op(torch, tp, synth, name, iters):
                 c = sets[it[0] % 3]
                 it[0] += 1
                 tp.tp_shard_sum(c["P"], c["Y"])
-        elif name == "c8_ce":
+        elif name == "vocab_ce":
             s = R.vocab_ce()
             fn = lambda: R.vocab_ce_step(s)
-        elif name.startswith("c5_"):
+        elif name in ("decode_col", "decode_row", "decode_col_noalloc"):
             s = R.decode()
-            k = {"c5_col": 0, "c5_row": 1, "c5_col_noalloc": 2}[name]
+            k = {"decode_col": 0, "decode_row": 1, "decode_col_noalloc": 2}[name]
             it = [0]
 
             def fn():
@@ -783,11 +783,11 @@ def cpu_baseline(synth, seconds):
     rows = 1024
     it = [0]
 
-    def c2():
+    def gpt2m_fwd():
         r0 = (it[0] * rows) % W.tokens
         it[0] += 1
         oracle.mlp_gelu(X[r0:r0 + rows], W1, W2)
-    sec, n = _time(c2, max(2 * share, 2.0))
+    sec, n = _time(gpt2m_fwd, max(2 * share, 2.0))
     f2s, f2 = 2.0 * 2 * rows * W.h * W.ffn, 2.0 * 2 * W.tokens * W.h * W.ffn
     rec("gpt2m_mlp_bf16_fwd", sec, f2s, f2, f"{rows} of {W.tokens} token rows per call", n)
     head = out["gpt2m_mlp_bf16_fwd"]
