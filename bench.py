@@ -59,43 +59,21 @@ def dev(t, torch):
     return torch.from_numpy(np.ascontiguousarray(t.f32)).to("cuda:0")
 
 
-class Timer:
-    """HIP events on the stream the library launches on (torch's current stream)."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def mark(self):
-        e = self.torch.cuda.Event(enable_timing=True)
-        e.record()
-        return e
-
-    def region(self, fn):
-        a = self.mark()
-        fn()
-        b = self.mark()
-        self.pairs.append((a, b))
-
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
-
-
 def timed(torch, step, steps, warmup):
+    """`warmup` untimed calls of step(), then the mean GPU time of `steps`
+    back-to-back calls between two HIP events on torch's current stream
+    (the launch stream), synchronised on both sides."""
     for _ in range(warmup):
-        step(None)
+        step()
     torch.cuda.synchronize()
-    kt = Timer(torch)
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t0.record()
     for _ in range(steps):
-        step(kt)
+        step()
     t1.record()
     torch.cuda.synchronize()
-    return t0.elapsed_time(t1) / steps, kt
+    return t0.elapsed_time(t1) / steps
 
 
 # --------------------------------------------------------------------------- headline
@@ -126,12 +104,9 @@ class Headline:
     def total(self):
         self.tp.tp_shard_sum(self.P, self.Y)
 
-    def step(self, kt):
+    def step(self):
         for i in range(self.n):
-            if kt is None:
-                self.col(i)
-            else:
-                kt.region(lambda i=i: self.col(i))
+            self.col(i)
             self.row(i)
         self.total()
 
@@ -218,10 +193,10 @@ def back_to_back_ms(torch, fn, iters):
 def headline(torch, hl, steps, warmup):
     """One step = the 9 launches of the 4-shard MLP layer + shard sum,
     enqueued back to back on the current stream (hl: a Headline)."""
-    ms, _ = timed(torch, lambda kt: hl.step(None), steps, warmup)
+    ms = timed(torch, lambda: hl.step(), steps, warmup)
     step_flops = 2 * hl.n * hl.gemm_flops
     col_ms = back_to_back_ms(torch, lambda: hl.col(0), max(steps, 50))
-    step_med, step_min = per_call_ms(torch, lambda: hl.step(None), steps)
+    step_med, step_min = per_call_ms(torch, lambda: hl.step(), steps)
     col_med, col_min = per_call_ms(torch, lambda: hl.col(0), max(steps, 50))
     return {
         "ms": ms, "tflops": step_flops / (ms * 1e-3) / 1e12, "step_flops": step_flops,
@@ -485,8 +460,8 @@ def rows(torch, tp, steps, warmup):
     s = R.swiglu()
     gf = graph_of(torch, lambda: (R.swiglu_col(s), R.swiglu_down(s)))
     gb = graph_of(torch, lambda: R.swiglu_bwd(s))
-    ms_f, _ = timed(torch, lambda kt: gf.replay(), s_ms, w_ms)
-    ms_b, _ = timed(torch, lambda kt: gb.replay(), s_ms, w_ms)
+    ms_f = timed(torch, lambda: gf.replay(), s_ms, w_ms)
+    ms_b = timed(torch, lambda: gb.replay(), s_ms, w_ms)
     flop_f, flop_b = 3 * s["flop_gemm"], 6 * s["flop_gemm"]
     out["llama_swiglu_fwd"] = {"ms": ms_f, "tflops": flop_f / ms_f / 1e9,
                                "frac_peak": flop_f / ms_f / 1e9 / PEAK_BF16_TFLOPS}
@@ -497,7 +472,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.gelu_mlp()
     gg = graph_of(torch, lambda: R.gelu_mlp_bwd(s))
-    ms_g, _ = timed(torch, lambda kt: gg.replay(), s_ms, w_ms)
+    ms_g = timed(torch, lambda: gg.replay(), s_ms, w_ms)
     out["gpt2m_gelu_mlp_bwd"] = {"ms": ms_g, "tflops": 4 * s["flop_gemm"] / ms_g / 1e9,
                                  "frac_peak": 4 * s["flop_gemm"] / ms_g / 1e9 / PEAK_BF16_TFLOPS,
                                  "note": "one GPT-2-medium shard (T 8192, h 1024, ffn 1024 per shard): "
@@ -506,7 +481,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.mha()
     ga = graph_of(torch, lambda: R.attn(s))
-    ms_a, _ = timed(torch, lambda kt: ga.replay(), s_ms, w_ms)
+    ms_a = timed(torch, lambda: ga.replay(), s_ms, w_ms)
     fa = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
     out["mha_heads_shard"] = {"ms": ms_a, "tflops": fa / ms_a / 1e9,
                               "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
@@ -514,7 +489,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.gqa()
     gq = graph_of(torch, lambda: R.gqa_attn(s))
-    ms_q, _ = timed(torch, lambda kt: gq.replay(), s_ms, w_ms)
+    ms_q = timed(torch, lambda: gq.replay(), s_ms, w_ms)
     fq = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
     out["gqa_heads_shard"] = {"ms": ms_q, "tflops": fq / ms_q / 1e9,
                               "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
@@ -523,7 +498,7 @@ def rows(torch, tp, steps, warmup):
     for key, kvl in (("mha_heads_shard_backward", None), ("gqa_heads_shard_backward", 2)):
         s = R.mha_bwd(kvl)
         gbw = graph_of(torch, lambda: R.attn_bwd(s))
-        ms_bw, _ = timed(torch, lambda kt: gbw.replay(), s_ms, w_ms)
+        ms_bw = timed(torch, lambda: gbw.replay(), s_ms, w_ms)
         fb = s["flop_bwd_gemm"] + s["flop_bwd_att"]
         out[key] = {"ms": ms_bw, "tflops": fb / ms_bw / 1e9, "frac_peak": fb / ms_bw / 1e9 / PEAK_BF16_TFLOPS,
                     "note": "dO, dWo, dWqkv, dX GEMMs + attention backward counted as 2.5x the causal "
@@ -531,7 +506,7 @@ def rows(torch, tp, steps, warmup):
         del s
     s = R.sp_ln()
     gl = graph_of(torch, lambda: R.sp_ln_step(s))
-    ms_l, _ = timed(torch, lambda kt: gl.replay(), s_ms, w_ms)
+    ms_l = timed(torch, lambda: gl.replay(), s_ms, w_ms)
     out["sp_reduce_scatter_layernorm"] = {"ms": ms_l, "bytes": s["bytes"], "gbs": s["bytes"] / ms_l / 1e6,
                                           "frac_hbm_peak": s["bytes"] / ms_l / 1e6 / PEAK_HBM_GBS,
                                           "note": "4 ranks x (sum of 4 fp32 partials + bias + residual, "
@@ -573,7 +548,7 @@ def rows(torch, tp, steps, warmup):
     del gs, sl
     s = R.vocab_ce()
     gc = graph_of(torch, lambda: R.vocab_ce_step(s))
-    ms_c, _ = timed(torch, lambda kt: gc.replay(), s_ms, w_ms)
+    ms_c = timed(torch, lambda: gc.replay(), s_ms, w_ms)
     out["vocab_parallel_cross_entropy"] = {"ms": ms_c, "bytes": s["bytes"], "gbs": s["bytes"] / ms_c / 1e6,
                                            "frac_hbm_peak": s["bytes"] / ms_c / 1e6 / PEAK_HBM_GBS,
                                            "note": "4 shards x [8192 x 32064] bf16 logits: row stats, "
@@ -582,7 +557,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.decode()
     gd = graph_of(torch, lambda: R.decode_step(s))
-    ms_d, _ = timed(torch, lambda kt: gd.replay(), s_ms, 3)
+    ms_d = timed(torch, lambda: gd.replay(), s_ms, 3)
     w_bytes = s["n"] * 2 * s["w_bytes"]
     out["decode_gemv"] = {"ms_step": ms_d, "weight_bytes": w_bytes,
                           "gbs": w_bytes / ms_d / 1e6, "frac_hbm_peak": w_bytes / ms_d / 1e6 / PEAK_HBM_GBS,
@@ -604,7 +579,7 @@ def run_op(torch, tp, synth, name, iters):
     elif name in ("gpt2m_col", "gpt2m_row", "gpt2m_sum", "gpt2m_step"):
         hl = Headline(torch, tp, synth)
         fn = {"gpt2m_col": lambda: hl.col(0), "gpt2m_row": lambda: hl.row(0), "gpt2m_sum": hl.total,
-              "gpt2m_step": lambda: hl.step(None)}[name]
+              "gpt2m_step": lambda: hl.step()}[name]
     else:
         R = Rows(torch, tp)
         if name in ("llama_swiglu_col", "llama_down", "llama_swiglu_bwd"):
