@@ -26,6 +26,8 @@ sequence-parallel reduce-scatter + LayerNorm, vocabulary-parallel
 cross-entropy, decode GEMV) unless --no-rows.
 """
 import argparse
+import contextlib
+import gc
 import json
 import os
 import sys
@@ -59,20 +61,36 @@ def dev(t, torch):
     return torch.from_numpy(np.ascontiguousarray(t.f32)).to("cuda:0")
 
 
+@contextlib.contextmanager
+def no_gc():
+    """Python's cyclic garbage collector paused (as timeit does): a collection
+    inside a timed region stalls the host thread that enqueues the launches,
+    and the GPU idles meanwhile.  No collection is forced on entry either:
+    the GPU would idle through it and its clock drop before the region."""
+    was = gc.isenabled()
+    gc.disable()
+    try:
+        yield
+    finally:
+        if was:
+            gc.enable()
+
+
 def timed(torch, step, steps, warmup):
     """`warmup` untimed calls of step(), then the mean GPU time of `steps`
     back-to-back calls between two HIP events on torch's current stream
     (the launch stream), synchronised on both sides."""
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(steps):
-        step()
-    t1.record()
-    torch.cuda.synchronize()
+    with no_gc():
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(steps):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
     return t0.elapsed_time(t1) / steps
 
 
@@ -115,14 +133,15 @@ def per_call_ms(torch, fn, iters):
     """Median and minimum GPU time of fn over iters calls, each bracketed by
     its own HIP events (outside the contract's timed region)."""
     pairs = []
-    for _ in range(iters):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        fn()
-        b.record()
-        pairs.append((a, b))
-    torch.cuda.synchronize()
+    with no_gc():
+        for _ in range(iters):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            pairs.append((a, b))
+        torch.cuda.synchronize()
     t = sorted(a.elapsed_time(b) for a, b in pairs)
     return t[len(t) // 2], t[0]
 
@@ -174,20 +193,44 @@ def graph_of(torch, fn):
     return g
 
 
-def back_to_back_ms(torch, fn, iters):
-    """Average GPU time per launch of fn over iters back-to-back launches
-    (HIP events on torch's current stream, which is the launch stream)."""
-    for _ in range(3):
-        fn()
-    torch.cuda.synchronize()
+def warm(torch, fn, ms=40.0):
+    """Enqueue fn back to back for about `ms` of GPU time and return without
+    waiting for it: from idle the engine clock needs ~20 ms of load to ramp,
+    and a timed region enqueued behind this backlog starts with the GPU busy,
+    so host-side stalls at its start (runtime housekeeping after a burst of
+    launches) do not show as idle time inside it."""
     a = torch.cuda.Event(enable_timing=True)
     b = torch.cuda.Event(enable_timing=True)
     a.record()
-    for _ in range(iters):
-        fn()
+    fn()
     b.record()
     torch.cuda.synchronize()
+    for _ in range(min(int(ms / max(a.elapsed_time(b), 1e-3)) + 1, 4000)):
+        fn()
+
+
+def back_to_back_ms(torch, fn, iters):
+    """Average GPU time per call of fn over iters back-to-back calls (HIP
+    events on torch's current stream, which is the launch stream), enqueued
+    behind warm()'s backlog: the steady-state rate of a loop of such calls."""
+    with no_gc():
+        warm(torch, fn)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(iters):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
     return a.elapsed_time(b) / iters
+
+
+def timed_row(torch, fn, steps, warmup):
+    """Mean GPU time of `steps` calls of fn, for a row other than the
+    headline: back_to_back_ms after `warmup` further untimed calls."""
+    for _ in range(warmup):
+        fn()
+    return back_to_back_ms(torch, fn, steps)
 
 
 def headline(torch, hl, steps, warmup):
@@ -460,8 +503,8 @@ def rows(torch, tp, steps, warmup):
     s = R.swiglu()
     gf = graph_of(torch, lambda: (R.swiglu_col(s), R.swiglu_down(s)))
     gb = graph_of(torch, lambda: R.swiglu_bwd(s))
-    ms_f = timed(torch, lambda: gf.replay(), s_ms, w_ms)
-    ms_b = timed(torch, lambda: gb.replay(), s_ms, w_ms)
+    ms_f = timed_row(torch, lambda: gf.replay(), s_ms, w_ms)
+    ms_b = timed_row(torch, lambda: gb.replay(), s_ms, w_ms)
     flop_f, flop_b = 3 * s["flop_gemm"], 6 * s["flop_gemm"]
     out["llama_swiglu_fwd"] = {"ms": ms_f, "tflops": flop_f / ms_f / 1e9,
                                "frac_peak": flop_f / ms_f / 1e9 / PEAK_BF16_TFLOPS}
@@ -472,7 +515,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.gelu_mlp()
     gg = graph_of(torch, lambda: R.gelu_mlp_bwd(s))
-    ms_g = timed(torch, lambda: gg.replay(), s_ms, w_ms)
+    ms_g = timed_row(torch, lambda: gg.replay(), s_ms, w_ms)
     out["gpt2m_gelu_mlp_bwd"] = {"ms": ms_g, "tflops": 4 * s["flop_gemm"] / ms_g / 1e9,
                                  "frac_peak": 4 * s["flop_gemm"] / ms_g / 1e9 / PEAK_BF16_TFLOPS,
                                  "note": "one GPT-2-medium shard (T 8192, h 1024, ffn 1024 per shard): "
@@ -481,7 +524,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.mha()
     ga = graph_of(torch, lambda: R.attn(s))
-    ms_a = timed(torch, lambda: ga.replay(), s_ms, w_ms)
+    ms_a = timed_row(torch, lambda: ga.replay(), s_ms, w_ms)
     fa = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
     out["mha_heads_shard"] = {"ms": ms_a, "tflops": fa / ms_a / 1e9,
                               "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
@@ -489,7 +532,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.gqa()
     gq = graph_of(torch, lambda: R.gqa_attn(s))
-    ms_q = timed(torch, lambda: gq.replay(), s_ms, w_ms)
+    ms_q = timed_row(torch, lambda: gq.replay(), s_ms, w_ms)
     fq = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
     out["gqa_heads_shard"] = {"ms": ms_q, "tflops": fq / ms_q / 1e9,
                               "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
@@ -498,7 +541,7 @@ def rows(torch, tp, steps, warmup):
     for key, kvl in (("mha_heads_shard_backward", None), ("gqa_heads_shard_backward", 2)):
         s = R.mha_bwd(kvl)
         gbw = graph_of(torch, lambda: R.attn_bwd(s))
-        ms_bw = timed(torch, lambda: gbw.replay(), s_ms, w_ms)
+        ms_bw = timed_row(torch, lambda: gbw.replay(), s_ms, w_ms)
         fb = s["flop_bwd_gemm"] + s["flop_bwd_att"]
         out[key] = {"ms": ms_bw, "tflops": fb / ms_bw / 1e9, "frac_peak": fb / ms_bw / 1e9 / PEAK_BF16_TFLOPS,
                     "note": "dO, dWo, dWqkv, dX GEMMs + attention backward counted as 2.5x the causal "
@@ -506,7 +549,7 @@ def rows(torch, tp, steps, warmup):
         del s
     s = R.sp_ln()
     gl = graph_of(torch, lambda: R.sp_ln_step(s))
-    ms_l = timed(torch, lambda: gl.replay(), s_ms, w_ms)
+    ms_l = timed_row(torch, lambda: gl.replay(), s_ms, w_ms)
     out["sp_reduce_scatter_layernorm"] = {"ms": ms_l, "bytes": s["bytes"], "gbs": s["bytes"] / ms_l / 1e6,
                                           "frac_hbm_peak": s["bytes"] / ms_l / 1e6 / PEAK_HBM_GBS,
                                           "note": "4 ranks x (sum of 4 fp32 partials + bias + residual, "
@@ -547,8 +590,8 @@ def rows(torch, tp, steps, warmup):
                 "HBM-resident inputs"}
     del gs, sl
     s = R.vocab_ce()
-    gc = graph_of(torch, lambda: R.vocab_ce_step(s))
-    ms_c = timed(torch, lambda: gc.replay(), s_ms, w_ms)
+    gv = graph_of(torch, lambda: R.vocab_ce_step(s))
+    ms_c = timed_row(torch, lambda: gv.replay(), s_ms, w_ms)
     out["vocab_parallel_cross_entropy"] = {"ms": ms_c, "bytes": s["bytes"], "gbs": s["bytes"] / ms_c / 1e6,
                                            "frac_hbm_peak": s["bytes"] / ms_c / 1e6 / PEAK_HBM_GBS,
                                            "note": "4 shards x [8192 x 32064] bf16 logits: row stats, "
@@ -557,7 +600,7 @@ def rows(torch, tp, steps, warmup):
     del s
     s = R.decode()
     gd = graph_of(torch, lambda: R.decode_step(s))
-    ms_d = timed(torch, lambda: gd.replay(), s_ms, 3)
+    ms_d = timed_row(torch, lambda: gd.replay(), s_ms, 3)
     w_bytes = s["n"] * 2 * s["w_bytes"]
     out["decode_gemv"] = {"ms_step": ms_d, "weight_bytes": w_bytes,
                           "gbs": w_bytes / ms_d / 1e6, "frac_hbm_peak": w_bytes / ms_d / 1e6 / PEAK_HBM_GBS,
