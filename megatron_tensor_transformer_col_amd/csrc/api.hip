@@ -801,12 +801,19 @@ int tp_mlp_shard_backward(int dtype, int act, int64_t M, int64_t K, int64_t Ni, 
     wu.C = dWup;
     TRY(hip_status(launch_gemm(w2, s), "dW2 GEMM"));
     TRY(hip_status(launch_gemm_tn_pair(w1, wu, s), "dW1 / dWup GEMMs"));
-  } else {
-    // one launch for both when they have the same shape (K == Ni) and split
-    TRY(hip_status(launch_gemm_tn_pair(w2, w1, s), "dW2 / dW1 GEMMs"));
   }
-  if (db1 != nullptr) {
-    float *cs = M > 0 ? reinterpret_cast<float *>(base + L.cs) : nullptr;  // M == 0: db1 = 0
+  float *cs = M > 0 ? reinterpret_cast<float *>(base + L.cs) : nullptr;  // M == 0: db1 = 0
+  bool db1_done = false;
+  if (!swiglu) {
+    // one launch for both when they have the same shape (K == Ni) and split;
+    // its partial-sum launch also adds db1's row-tile partials when the
+    // recompute wrote them
+    ColsumJob cj;
+    cj.rows = db1_tiles; cj.N = Ni; cj.part = cs; cj.db = db1;
+    const bool with_db1 = db1 != nullptr && db1_tiles > 0;
+    TRY(hip_status(launch_gemm_tn_pair(w2, w1, s, with_db1 ? &cj : nullptr, &db1_done), "dW2 / dW1 GEMMs"));
+  }
+  if (db1 != nullptr && !db1_done) {
     if (db1_tiles > 0)
       TRY(hip_status(launch_colsum_final(db1_tiles, Ni, cs, db1, s), "db1"));
     else

@@ -360,8 +360,11 @@ static hipError_t launch_lds(const GemmArgs &a, hipStream_t s) {
 // Both weight gradients of a backward in one launch: K-range splits of the
 // two products share the grid (rows [0, S) the first, [S, 2S) the second),
 // so that narrow outputs fill two workgroups per CU, then one launch adds
-// each product's partials in split order.
-hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream_t s) {
+// each product's partials in split order (and takes on the column sum cj,
+// if given, in spare workgroups of that launch).
+hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream_t s, const ColsumJob *cj,
+                               bool *cj_done) {
+  if (cj_done != nullptr) *cj_done = false;
   auto separate = [&]() -> hipError_t {
     const hipError_t e = launch_gemm(a0, s);
     if (e != hipSuccess) return e;
@@ -394,8 +397,10 @@ hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream
   if (e != hipSuccess) return e;
   const float *parts[16];
   for (int z = 0; z < 2 * S; ++z) parts[z] = a0.part + (int64_t)z * b.zstride;
-  return launch_shard_sum_pair(a0.M, a0.N, S, parts, a0.N, static_cast<float *>(a0.C), a0.ldc,
-                               static_cast<float *>(a1.C), a1.ldc, s);
+  const hipError_t e2 = launch_shard_sum_pair(a0.M, a0.N, S, parts, a0.N, static_cast<float *>(a0.C), a0.ldc,
+                                              static_cast<float *>(a1.C), a1.ldc, s, cj);
+  if (e2 == hipSuccess && cj != nullptr && cj_done != nullptr) *cj_done = true;
+  return e2;
 }
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s) {

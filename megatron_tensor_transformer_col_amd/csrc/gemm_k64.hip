@@ -371,6 +371,27 @@ gemm_k64_kernel(GemmParams pin) {
     interleave();
   };
 
+  // activation backward with four waves: the epilogue's dH tile is loaded
+  // (coalesced 16-byte row chunks, DHE per thread) during the main loop
+  constexpr bool DH_EARLY = STAGED3 && NWV == 4 && STAGES == 2;
+  constexpr int DH_CPR = BNO * 2 / 16;
+  constexpr int DHE = DH_EARLY ? (BM * DH_CPR + NWV * 64 - 1) / (NWV * 64) : 1;
+  uint4 dhe[DHE];
+  auto load_dh_early = [&]() {
+    if constexpr (DH_EARLY) {
+#pragma unroll
+      for (int k = 0; k < DHE; ++k) {
+        const int c = (int)threadIdx.x + k * NWV * 64;
+        const int rl = c / DH_CPR, cc = c % DH_CPR;
+        const int row = m0 + rl, col = n0 + cc * 8;
+        dhe[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < BM * DH_CPR && row < M && col < N)
+          dhe[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
+      }
+    }
+  };
+  bool dh_loaded = false;
+
   if constexpr (NWV == 4) {
 #pragma unroll
     for (int s = 0; s < STAGES; ++s)
@@ -380,9 +401,32 @@ gemm_k64_kernel(GemmParams pin) {
     __syncthreads();
     Frags F0, F1;
     load_chunk(F0, 0, 0);
-    for (int kt = 0; kt < nk - 1; ++kt) {
-      half0(kt, F0, F1);
-      half1(kt, F1, F0);
+    if constexpr (DH_EARLY) {
+      // the dH loads go out right after the last slab's DMA (issued in
+      // half1(nk - 3)) and are waited for with it in half1(nk - 2): their
+      // latency passes under the last slabs' MFMAs instead of opening the
+      // epilogue
+      int kt = 0;
+      if (nk >= 3) {
+        for (; kt < nk - 3; ++kt) {
+          half0(kt, F0, F1);
+          half1(kt, F1, F0);
+        }
+        half0(kt, F0, F1);
+        half1(kt, F1, F0);
+        load_dh_early();
+        dh_loaded = true;
+        ++kt;
+      }
+      for (; kt < nk - 1; ++kt) {
+        half0(kt, F0, F1);
+        half1(kt, F1, F0);
+      }
+    } else {
+      for (int kt = 0; kt < nk - 1; ++kt) {
+        half0(kt, F0, F1);
+        half1(kt, F1, F0);
+      }
     }
     half0(nk - 1, F0, F1);
     mma(F1);
@@ -483,16 +527,24 @@ gemm_k64_kernel(GemmParams pin) {
     char *out = smem + BM * SR3;
     float *red = reinterpret_cast<float *>(smem + 2 * BM * SR3);  // [16][BNO] (CSUM)
     // every dH load of the thread is in flight before the first one is
-    // waited on (one memory latency per tile, not one per chunk)
+    // waited on (one memory latency per tile, not one per chunk), unless
+    // the main loop has loaded the tile already
     uint4 dhv[DHN];
+    if constexpr (DH_EARLY) {
+      static_assert(DHE == DHN, "dH chunks per thread");
+      if (!dh_loaded) load_dh_early();
 #pragma unroll
-    for (int k = 0; k < DHN; ++k) {
-      const int c = (int)threadIdx.x + k * NWV * 64;
-      const int rl = c / CPR, cc = c % CPR;
-      const int row = m0 + rl, col = n0 + cc * 8;
-      dhv[k] = make_uint4(0u, 0u, 0u, 0u);
-      if (c < BM * CPR && row < M && col < N)
-        dhv[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
+      for (int k = 0; k < DHN; ++k) dhv[k] = dhe[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < DHN; ++k) {
+        const int c = (int)threadIdx.x + k * NWV * 64;
+        const int rl = c / CPR, cc = c % CPR;
+        const int row = m0 + rl, col = n0 + cc * 8;
+        dhv[k] = make_uint4(0u, 0u, 0u, 0u);
+        if (c < BM * CPR && row < M && col < N)
+          dhv[k] = *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(p.D) + (int64_t)row * p.ldd + col);
+      }
     }
     if (p.bias != nullptr) {
       float bv[TNO][4];

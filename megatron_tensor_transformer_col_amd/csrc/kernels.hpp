@@ -60,10 +60,21 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs &a, hipStream_t s);
+// db[c] = sum over rows r < rows of part[r][c] (launch_colsum_final's work),
+// for a launch that can take it on beside its own
+struct ColsumJob {
+  int rows = 0;
+  int64_t N = 0;
+  const float *part = nullptr;
+  float *db = nullptr;
+};
 // Two bf16 TN fp32 products of the same shape (a0.C = A0^T B0, a1.C =
 // A1^T B1): one K-split launch for both when a0.part holds their partials,
-// else two launch_gemm calls.
-hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream_t s);
+// else two launch_gemm calls.  cj (optional): a column sum whose inputs are
+// complete before this call; when the split path's partial-sum launch has
+// run it too, *cj_done is set (else the caller launches it).
+hipError_t launch_gemm_tn_pair(const GemmArgs &a0, const GemmArgs &a1, hipStream_t s,
+                               const ColsumJob *cj = nullptr, bool *cj_done = nullptr);
 
 // Decode GEMV (M <= 16): y = act(x W + bias) with split-K partials in ws.
 struct GemvArgs {
@@ -91,9 +102,11 @@ size_t gemv_noalloc_max_bytes();
 hipError_t launch_shard_sum(int out_dtype, int64_t M, int64_t N, int n, const float *const *parts,
                             int64_t ldp, const float *bias, void *Y, int64_t ldy, hipStream_t s);
 // Two such sums in one launch (fp32 outputs, no bias): Y0 = sum_i P_i,
-// Y1 = sum_i P_{n+i} for i < n.
+// Y1 = sum_i P_{n+i} for i < n; with cj, the same launch also does that
+// column sum (in launch_colsum_final's order: bitwise the same db).
 hipError_t launch_shard_sum_pair(int64_t M, int64_t N, int n, const float *const *parts, int64_t ldp,
-                                 float *Y0, int64_t ldy0, float *Y1, int64_t ldy1, hipStream_t s);
+                                 float *Y0, int64_t ldy0, float *Y1, int64_t ldy1, hipStream_t s,
+                                 const ColsumJob *cj = nullptr);
 
 // Head-local flash attention over a packed [Q|K|V] buffer (bf16, d = 128).
 // lse (optional, [b][heads_local][s] fp32): log2 of each query row's softmax

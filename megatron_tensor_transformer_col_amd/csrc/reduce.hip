@@ -41,14 +41,59 @@ shard_sum_kernel(PartialPtrs pp, int n, int64_t M, int64_t N4, int64_t ldp, cons
   }
 }
 
+// db[c] = sum over rows y < splits of part[y][c]: 16 lanes of a wave per
+// column, lane l adding rows l, l + 16, ... in order, then the 16 lane
+// sums added in lane order (a fixed order; one round trip of loads per
+// 16 rows instead of a chain over all of them).  Block b covers columns
+// 16 b .. 16 b + 15; every lane of the block takes part (the shuffles).
+__device__ __forceinline__ void colsum_final_block(int64_t b, int splits, int64_t N, const float *__restrict__ part,
+                                                   float *__restrict__ db) {
+  const int lane = threadIdx.x & 63, l = lane & 15;
+  const int64_t c = (b * 256 + threadIdx.x) >> 4;  // 4 columns per wave
+  float t = 0.f;
+  if (c < N) {
+    for (int y0 = 0; y0 < splits; y0 += 64) {
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int y = y0 + 16 * j + l;
+        v[j] = y < splits ? part[(int64_t)y * N + c] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (y0 + 16 * j + l < splits) t += v[j];
+    }
+  }
+  // lane sums in lane order: lane 0 of each 16-lane group collects 1..15
+  float tot = t;
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    const float o = __shfl(t, (lane & ~15) + k);
+    if (l == 0) tot += o;
+  }
+  if (l == 0 && c < N) db[c] = tot;
+}
+
+__global__ void __launch_bounds__(256)
+colsum_final_kernel(int splits, int64_t N, const float *__restrict__ part, float *__restrict__ db) {
+  colsum_final_block(blockIdx.x, splits, N, part, db);
+}
+
 // Two sums of n partials each (fp32 out): element v of the combined range
 // [0, 2 M N4) belongs to sum g = v / (M N4), whose terms are P_{g n + i}.
+// Blocks past the first sum_blocks do colsum_final_block's work instead
+// (cs_rows rows of cs_part, cs_N columns, into db).
 __global__ void __launch_bounds__(256)
 shard_sum_pair_kernel(PartialPtrs pp, int n, int64_t M, int64_t N4, int64_t ldp, float *Y0, int64_t ldy0,
-                      float *Y1, int64_t ldy1) {
+                      float *Y1, int64_t ldy1, int sum_blocks, int cs_rows, int64_t cs_N,
+                      const float *cs_part, float *db) {
+  if ((int)blockIdx.x >= sum_blocks) {
+    colsum_final_block((int64_t)blockIdx.x - sum_blocks, cs_rows, cs_N, cs_part, db);
+    return;
+  }
   const int64_t one = M * N4;
   for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < 2 * one;
-       v += (int64_t)gridDim.x * blockDim.x) {
+       v += (int64_t)sum_blocks * blockDim.x) {
     const int g = v >= one ? 1 : 0;
     const int64_t w = v - g * one;
     const int64_t row = w / N4, c = (w - row * N4) * 4;
@@ -63,16 +108,23 @@ shard_sum_pair_kernel(PartialPtrs pp, int n, int64_t M, int64_t N4, int64_t ldp,
   }
 }
 
+static unsigned colsum_final_blocks(int64_t N) { return (unsigned)((N * 16 + 255) / 256); }
+
 hipError_t launch_shard_sum_pair(int64_t M, int64_t N, int n, const float *const *parts, int64_t ldp,
-                                 float *Y0, int64_t ldy0, float *Y1, int64_t ldy1, hipStream_t s) {
+                                 float *Y0, int64_t ldy0, float *Y1, int64_t ldy1, hipStream_t s,
+                                 const ColsumJob *cj) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (n < 1 || 2 * n > kMaxShards || N % 4) return hipErrorInvalidValue;
+  if (cj != nullptr && (cj->rows < 0 || cj->N <= 0)) return hipErrorInvalidValue;
   PartialPtrs pp;
   for (int i = 0; i < kMaxShards; ++i) pp.p[i] = parts[i < 2 * n ? i : 0];
   const int64_t N4 = N / 4;
   const int64_t want = (2 * M * N4 + 255) / 256;
   const unsigned grid = (unsigned)(want < 2048 ? want : 2048);
-  hipLaunchKernelGGL(shard_sum_pair_kernel, dim3(grid), dim3(256), 0, s, pp, n, M, N4, ldp, Y0, ldy0, Y1, ldy1);
+  const unsigned extra = cj != nullptr ? colsum_final_blocks(cj->N) : 0u;
+  hipLaunchKernelGGL(shard_sum_pair_kernel, dim3(grid + extra), dim3(256), 0, s, pp, n, M, N4, ldp, Y0, ldy0, Y1,
+                     ldy1, (int)grid, cj != nullptr ? cj->rows : 0, cj != nullptr ? cj->N : (int64_t)0,
+                     cj != nullptr ? cj->part : (const float *)nullptr, cj != nullptr ? cj->db : (float *)nullptr);
   return hipGetLastError();
 }
 
@@ -173,42 +225,10 @@ colsum_partial_kernel(int64_t M, int64_t N, const T *__restrict__ dZ, int64_t ld
   }
 }
 
-// db[c] = sum over rows y < splits of part[y][c]: 16 lanes of a wave per
-// column, lane l adding rows l, l + 16, ... in order, then the 16 lane
-// sums added in lane order (a fixed order; one round trip of loads per
-// 16 rows instead of a chain over all of them)
-__global__ void __launch_bounds__(256)
-colsum_final_kernel(int splits, int64_t N, const float *__restrict__ part, float *__restrict__ db) {
-  const int lane = threadIdx.x & 63, l = lane & 15;
-  const int64_t c = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 4;  // 16 columns per wave
-  float t = 0.f;
-  if (c < N) {
-    for (int y0 = 0; y0 < splits; y0 += 64) {
-      float v[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int y = y0 + 16 * j + l;
-        v[j] = y < splits ? part[(int64_t)y * N + c] : 0.f;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (y0 + 16 * j + l < splits) t += v[j];
-    }
-  }
-  // lane sums in lane order: lane 0 of each 16-lane group collects 1..15
-  float tot = t;
-#pragma unroll
-  for (int k = 1; k < 16; ++k) {
-    const float o = __shfl(t, (lane & ~15) + k);
-    if (l == 0) tot += o;
-  }
-  if (l == 0 && c < N) db[c] = tot;
-}
-
 hipError_t launch_colsum_final(int rows, int64_t N, const float *part, float *db, hipStream_t s) {
   if (N <= 0) return hipSuccess;
   if (rows < 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N * 16 + 255) / 256)), dim3(256), 0, s, rows, N, part, db);
+  hipLaunchKernelGGL(colsum_final_kernel, dim3(colsum_final_blocks(N)), dim3(256), 0, s, rows, N, part, db);
   return hipGetLastError();
 }
 
@@ -231,7 +251,7 @@ hipError_t launch_colsum(int dtype, int64_t M, int64_t N, const void *dZ, int64_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(colsum_final_kernel, dim3((unsigned)((N * 16 + 255) / 256)), dim3(256), 0, s, splits, N,
+  hipLaunchKernelGGL(colsum_final_kernel, dim3(colsum_final_blocks(N)), dim3(256), 0, s, splits, N,
                      part, db);
   return hipGetLastError();
 }
