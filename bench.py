@@ -495,58 +495,17 @@ class Rows:
         self.tp.tp_shard_sum(s["P"], s["Y"])
 
 
+ROW_ORDER = ["llama_swiglu_fwd", "llama_swiglu_bwd", "gpt2m_gelu_mlp_bwd", "mha_heads_shard", "gqa_heads_shard", "mha_heads_shard_backward", "gqa_heads_shard_backward", "sp_reduce_scatter_layernorm", "shard_sum_cold", "sp_reduce_scatter_layernorm_cold", "vocab_parallel_cross_entropy", "decode_gemv"]
+
+
 def rows(torch, tp, steps, warmup):
     R = Rows(torch, tp)
     out = {}
     s_ms = min(steps, 20)
     w_ms = min(warmup, 10)
-    s = R.swiglu()
-    gf = graph_of(torch, lambda: (R.swiglu_col(s), R.swiglu_down(s)))
-    gb = graph_of(torch, lambda: R.swiglu_bwd(s))
-    ms_f = timed_row(torch, lambda: gf.replay(), s_ms, w_ms)
-    ms_b = timed_row(torch, lambda: gb.replay(), s_ms, w_ms)
-    flop_f, flop_b = 3 * s["flop_gemm"], 6 * s["flop_gemm"]
-    out["llama_swiglu_fwd"] = {"ms": ms_f, "tflops": flop_f / ms_f / 1e9,
-                               "frac_peak": flop_f / ms_f / 1e9 / PEAK_BF16_TFLOPS}
-    out["llama_swiglu_bwd"] = {"ms": ms_b, "tflops": flop_b / ms_b / 1e9,
-                               "frac_peak": flop_b / ms_b / 1e9 / PEAK_BF16_TFLOPS,
-                               "note": "algorithmic flops (dgrad x3 + wgrad x3); the Z recompute "
-                                       "(+2 GEMMs) is not counted"}
-    del s
-    s = R.gelu_mlp()
-    gg = graph_of(torch, lambda: R.gelu_mlp_bwd(s))
-    ms_g = timed_row(torch, lambda: gg.replay(), s_ms, w_ms)
-    out["gpt2m_gelu_mlp_bwd"] = {"ms": ms_g, "tflops": 4 * s["flop_gemm"] / ms_g / 1e9,
-                                 "frac_peak": 4 * s["flop_gemm"] / ms_g / 1e9 / PEAK_BF16_TFLOPS,
-                                 "note": "one GPT-2-medium shard (T 8192, h 1024, ffn 1024 per shard): "
-                                         "algorithmic flops of dH, dW2, dW1, dX; the Z recompute and db1 "
-                                         "are not counted"}
-    del s
-    s = R.mha()
-    ga = graph_of(torch, lambda: R.attn(s))
-    ms_a = timed_row(torch, lambda: ga.replay(), s_ms, w_ms)
-    fa = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
-    out["mha_heads_shard"] = {"ms": ms_a, "tflops": fa / ms_a / 1e9,
-                              "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
-                              "note": "QKV GEMM + causal attention (4*d*s(s+1)/2 per head) + W_o GEMM"}
-    del s
-    s = R.gqa()
-    gq = graph_of(torch, lambda: R.gqa_attn(s))
-    ms_q = timed_row(torch, lambda: gq.replay(), s_ms, w_ms)
-    fq = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
-    out["gqa_heads_shard"] = {"ms": ms_q, "tflops": fq / ms_q / 1e9,
-                              "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
-                              "note": "8 query + 2 kv heads: QKV GEMM + causal attention + W_o GEMM"}
-    del s
-    for key, kvl in (("mha_heads_shard_backward", None), ("gqa_heads_shard_backward", 2)):
-        s = R.mha_bwd(kvl)
-        gbw = graph_of(torch, lambda: R.attn_bwd(s))
-        ms_bw = timed_row(torch, lambda: gbw.replay(), s_ms, w_ms)
-        fb = s["flop_bwd_gemm"] + s["flop_bwd_att"]
-        out[key] = {"ms": ms_bw, "tflops": fb / ms_bw / 1e9, "frac_peak": fb / ms_bw / 1e9 / PEAK_BF16_TFLOPS,
-                    "note": "dO, dWo, dWqkv, dX GEMMs + attention backward counted as 2.5x the causal "
-                            "forward (S recompute, dP, dV, dK, dQ); the kernels recompute S and dP twice"}
-        del s
+    # the HBM-bound rows first and the matrix-core ones last, so that the
+    # headline, timed next, starts with the engine clock at its loaded
+    # steady state rather than where the memory-bound rows left it
     s = R.sp_ln()
     gl = graph_of(torch, lambda: R.sp_ln_step(s))
     ms_l = timed_row(torch, lambda: gl.replay(), s_ms, w_ms)
@@ -606,7 +565,55 @@ def rows(torch, tp, steps, warmup):
                           "gbs": w_bytes / ms_d / 1e6, "frac_hbm_peak": w_bytes / ms_d / 1e6 / PEAK_HBM_GBS,
                           "note": "16 GEMVs (8 shards x col + row) + shard sum per HIP-graph replay; "
                                   "GB/s counts weight bytes only"}
-    return out
+    del s
+    s = R.gelu_mlp()
+    gg = graph_of(torch, lambda: R.gelu_mlp_bwd(s))
+    ms_g = timed_row(torch, lambda: gg.replay(), s_ms, w_ms)
+    out["gpt2m_gelu_mlp_bwd"] = {"ms": ms_g, "tflops": 4 * s["flop_gemm"] / ms_g / 1e9,
+                                 "frac_peak": 4 * s["flop_gemm"] / ms_g / 1e9 / PEAK_BF16_TFLOPS,
+                                 "note": "one GPT-2-medium shard (T 8192, h 1024, ffn 1024 per shard): "
+                                         "algorithmic flops of dH, dW2, dW1, dX; the Z recompute and db1 "
+                                         "are not counted"}
+    del s
+    s = R.mha()
+    ga = graph_of(torch, lambda: R.attn(s))
+    ms_a = timed_row(torch, lambda: ga.replay(), s_ms, w_ms)
+    fa = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
+    out["mha_heads_shard"] = {"ms": ms_a, "tflops": fa / ms_a / 1e9,
+                              "frac_peak": fa / ms_a / 1e9 / PEAK_BF16_TFLOPS,
+                              "note": "QKV GEMM + causal attention (4*d*s(s+1)/2 per head) + W_o GEMM"}
+    del s
+    s = R.gqa()
+    gq = graph_of(torch, lambda: R.gqa_attn(s))
+    ms_q = timed_row(torch, lambda: gq.replay(), s_ms, w_ms)
+    fq = s["flop_qkv"] + s["flop_att"] + s["flop_o"]
+    out["gqa_heads_shard"] = {"ms": ms_q, "tflops": fq / ms_q / 1e9,
+                              "frac_peak": fq / ms_q / 1e9 / PEAK_BF16_TFLOPS,
+                              "note": "8 query + 2 kv heads: QKV GEMM + causal attention + W_o GEMM"}
+    del s
+    for key, kvl in (("mha_heads_shard_backward", None), ("gqa_heads_shard_backward", 2)):
+        s = R.mha_bwd(kvl)
+        gbw = graph_of(torch, lambda: R.attn_bwd(s))
+        ms_bw = timed_row(torch, lambda: gbw.replay(), s_ms, w_ms)
+        fb = s["flop_bwd_gemm"] + s["flop_bwd_att"]
+        out[key] = {"ms": ms_bw, "tflops": fb / ms_bw / 1e9, "frac_peak": fb / ms_bw / 1e9 / PEAK_BF16_TFLOPS,
+                    "note": "dO, dWo, dWqkv, dX GEMMs + attention backward counted as 2.5x the causal "
+                            "forward (S recompute, dP, dV, dK, dQ); the kernels recompute S and dP twice"}
+        del s
+    s = R.swiglu()
+    gf = graph_of(torch, lambda: (R.swiglu_col(s), R.swiglu_down(s)))
+    gb = graph_of(torch, lambda: R.swiglu_bwd(s))
+    ms_f = timed_row(torch, lambda: gf.replay(), s_ms, w_ms)
+    ms_b = timed_row(torch, lambda: gb.replay(), s_ms, w_ms)
+    flop_f, flop_b = 3 * s["flop_gemm"], 6 * s["flop_gemm"]
+    out["llama_swiglu_fwd"] = {"ms": ms_f, "tflops": flop_f / ms_f / 1e9,
+                               "frac_peak": flop_f / ms_f / 1e9 / PEAK_BF16_TFLOPS}
+    out["llama_swiglu_bwd"] = {"ms": ms_b, "tflops": flop_b / ms_b / 1e9,
+                               "frac_peak": flop_b / ms_b / 1e9 / PEAK_BF16_TFLOPS,
+                               "note": "algorithmic flops (dgrad x3 + wgrad x3); the Z recompute "
+                                       "(+2 GEMMs) is not counted"}
+    del s
+    return {k: out[k] for k in ROW_ORDER}
 
 
 # --------------------------------------------------------------------------- single ops
