@@ -287,7 +287,23 @@ def other_rooflines(torch, tp):
         "achieved": round(wb / ms / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
         "frac": round(wb / ms / 1e6 / PEAK_HBM_GBS, 4), "avg_call_us": round(ms * 1e3, 2),
         "weight_bytes_per_call": wb, "noalloc_avg_call_us": round(ms_na * 1e3, 2),
-        "traffic": traffic_record(GEMV_TRAFFIC_PROFILE, GEMV_TRAFFIC_SOURCES),
+        "traffic": traffic_record(GEMV_TRAFFIC_PROFILE, GEMV_TRAFFIC_SOURCES, "(column GEMV)"),
+        "traffic_unit": "HBM bytes per call, split-K pass + finalize (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                        "copy-calibrated)"}
+    R.decode_pack(s)
+
+    def col_packed():
+        i = it[0] % s["n"]
+        it[0] += 1
+        tp.tp_decode_linear_packed(s["x"], s["W1p"][i], s["H"][i], act="gelu")
+    ms_p = back_to_back_ms(torch, col_packed, 64)
+    out["decode_gemv_packed"] = {
+        "bound": "hbm", "kernel": "decode column GEMV on 64-column weight panels (tp_decode_linear_packed: "
+                                  "split-K pass + finalize, 16 x 8192 x 3584, GELU)",
+        "achieved": round(wb / ms_p / 1e6, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+        "frac": round(wb / ms_p / 1e6 / PEAK_HBM_GBS, 4), "avg_call_us": round(ms_p * 1e3, 2),
+        "weight_bytes_per_call": wb,
+        "traffic": traffic_record(GEMV_TRAFFIC_PROFILE, GEMV_TRAFFIC_SOURCES, "(packed column GEMV)"),
         "traffic_unit": "HBM bytes per call, split-K pass + finalize (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                         "copy-calibrated)"}
     return out
@@ -488,6 +504,20 @@ class Rows:
         s["w_bytes"] = 2.0 * h * f
         return s
 
+    def decode_pack(self, s):
+        """Panel copies of the decode weights (packed once, as a server does
+        when it loads them; outside every timed region)."""
+        s["W1p"] = [self.tp.tp_decode_pack_weight(w) for w in s["W1"]]
+        s["W2p"] = [self.tp.tp_decode_pack_weight(w) for w in s["W2"]]
+        self.torch.cuda.synchronize()
+        return s
+
+    def decode_step_packed(self, s):
+        for i in range(s["n"]):
+            self.tp.tp_decode_linear_packed(s["x"], s["W1p"][i], s["H"][i], act="gelu")
+            self.tp.tp_decode_linear_packed(s["H"][i], s["W2p"][i], s["P"][i], act="none")
+        self.tp.tp_shard_sum(s["P"], s["Y"])
+
     def decode_step(self, s):
         for i in range(s["n"]):
             self.tp.tp_col_linear_gelu(s["x"], s["W1"][i], s["H"][i])
@@ -495,7 +525,7 @@ class Rows:
         self.tp.tp_shard_sum(s["P"], s["Y"])
 
 
-ROW_ORDER = ["llama_swiglu_fwd", "llama_swiglu_bwd", "gpt2m_gelu_mlp_bwd", "mha_heads_shard", "gqa_heads_shard", "mha_heads_shard_backward", "gqa_heads_shard_backward", "sp_reduce_scatter_layernorm", "shard_sum_cold", "sp_reduce_scatter_layernorm_cold", "vocab_parallel_cross_entropy", "decode_gemv"]
+ROW_ORDER = ["llama_swiglu_fwd", "llama_swiglu_bwd", "gpt2m_gelu_mlp_bwd", "mha_heads_shard", "gqa_heads_shard", "mha_heads_shard_backward", "gqa_heads_shard_backward", "sp_reduce_scatter_layernorm", "shard_sum_cold", "sp_reduce_scatter_layernorm_cold", "vocab_parallel_cross_entropy", "decode_gemv", "decode_gemv_packed"]
 
 
 def rows(torch, tp, steps, warmup):
@@ -565,6 +595,13 @@ def rows(torch, tp, steps, warmup):
                           "gbs": w_bytes / ms_d / 1e6, "frac_hbm_peak": w_bytes / ms_d / 1e6 / PEAK_HBM_GBS,
                           "note": "16 GEMVs (8 shards x col + row) + shard sum per HIP-graph replay; "
                                   "GB/s counts weight bytes only"}
+    R.decode_pack(s)
+    gp = graph_of(torch, lambda: R.decode_step_packed(s))
+    ms_p = timed_row(torch, lambda: gp.replay(), s_ms, 3)
+    out["decode_gemv_packed"] = {"ms_step": ms_p, "weight_bytes": w_bytes,
+                                 "gbs": w_bytes / ms_p / 1e6, "frac_hbm_peak": w_bytes / ms_p / 1e6 / PEAK_HBM_GBS,
+                                 "note": "as decode_gemv, on the weights packed once into 64-column panels "
+                                         "(tp_decode_pack_weight, outside the timed region)"}
     del s
     s = R.gelu_mlp()
     gg = graph_of(torch, lambda: R.gelu_mlp_bwd(s))
@@ -670,9 +707,12 @@ def run_op(torch, tp, synth, name, iters):
         elif name == "vocab_ce":
             s = R.vocab_ce()
             fn = lambda: R.vocab_ce_step(s)
-        elif name in ("decode_col", "decode_row", "decode_col_noalloc"):
+        elif name in ("decode_col", "decode_row", "decode_col_noalloc", "decode_col_packed", "decode_row_packed"):
             s = R.decode()
-            k = {"decode_col": 0, "decode_row": 1, "decode_col_noalloc": 2}[name]
+            k = {"decode_col": 0, "decode_row": 1, "decode_col_noalloc": 2, "decode_col_packed": 3,
+                 "decode_row_packed": 4}[name]
+            if k >= 3:
+                R.decode_pack(s)
             it = [0]
 
             def fn():
@@ -682,6 +722,10 @@ def run_op(torch, tp, synth, name, iters):
                     tp.tp_col_linear_gelu(s["x"], s["W1"][i], s["H"][i])
                 elif k == 2:
                     tp.tp_col_linear_gelu_noalloc(s["x"], s["W1"][i], s["H"][i])
+                elif k == 3:
+                    tp.tp_decode_linear_packed(s["x"], s["W1p"][i], s["H"][i], act="gelu")
+                elif k == 4:
+                    tp.tp_decode_linear_packed(s["H"][i], s["W2p"][i], s["P"][i], act="none")
                 else:
                     tp.tp_row_linear_partial(s["H"][i], s["W2"][i], s["P"][i])
         else:
@@ -715,14 +759,16 @@ def col_gemm_traffic():
     return traffic_record(TRAFFIC_PROFILE, TRAFFIC_SOURCES)
 
 
-def traffic_record(profile, sources):
+def traffic_record(profile, sources, kernel=None):
     """HBM bytes per call from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     record (KiB per call, summed over the call's dispatches, scaled by the
     factors a 1 GiB copy gave), or None when the record is missing or the
-    kernel's sources changed since the counters were taken."""
+    kernel's sources changed since the counters were taken.  ``kernel``
+    picks the record whose kernel name contains it (default: the first)."""
     import hashlib
     try:
-        line = next(l for l in open(profile) if l.startswith("traffic-record:"))
+        line = next(l for l in open(profile) if l.startswith("traffic-record:")
+                    and (kernel is None or kernel in json.loads(l.split(":", 1)[1]).get("kernel", "")))
         rec = json.loads(line.split(":", 1)[1])
         h = hashlib.sha256()
         for f in sources:

@@ -135,6 +135,49 @@ int tp_row_linear_partial(int dtype, int64_t M, int64_t Ki, int64_t N,
 size_t tp_row_linear_partial_workspace(int dtype, int64_t M, int64_t Ki, int64_t N);
 
 /*
+ * Decode linear on a pre-packed weight.  In the decode phase every request
+ * adds one token, so a linear layer reads its whole weight once per token
+ * for 2 * M flops per weight (parallelism overview post, Prefill-Decode
+ * 分离 -> Decode 阶段 -> 线性层: memory-bound); the weight does not change
+ * between tokens, so it can be stored once in the order the weight-streaming
+ * kernel reads it.
+ *
+ * tp_decode_pack_weight: Wp = panels of 64 columns, each holding every row:
+ *     Wp[(s * Kp + k) * 64 + c] = W[k][64 s + c]     (bf16)
+ * for panels s < ceil(N / 64), rows k < Kp = K rounded up to a multiple of
+ * 64, columns c < 64; entries past K or N are zero.  Wp must hold
+ * tp_decode_packed_weight_bytes(K, N) bytes (16-byte aligned), and the call
+ * writes all of them.  W [K x N] ldw bf16 is row-major as everywhere else.
+ *
+ * tp_decode_linear_packed: the decode path of tp_col_linear_gelu /
+ * tp_row_linear_partial with W read from its panels:
+ *     Y = act(X @ W + bias)   out_dtype TP_BF16, act TP_ACT_NONE / TP_ACT_GELU_ERF
+ *     Y = X @ W (+ bias)      out_dtype TP_F32 (row-parallel partial), act NONE
+ *   X  [M x K] ldx bf16, 1 <= M <= 16 (M == 0: no-op)
+ *   Wp tp_decode_pack_weight's output for the same K, N (wp_bytes its size)
+ *   Y  [M x N] ldy, bf16 or fp32 (out_dtype)
+ *   ws tp_decode_linear_packed_workspace(M, K, N) bytes, 256-byte aligned
+ *      (split-K partial sums; contents on entry do not matter)
+ * Each workgroup's share of a panel is one contiguous run of memory (in the
+ * row-major layout it is 128 bytes from each of its rows).  The sums are
+ * taken in the same order as the row-major decode path, so for the same X,
+ * W and bias both give identical results.  dtype is bf16 only; M > 16, fp32
+ * output with an activation, or a Wp smaller than the panels need return an
+ * error before any launch.
+ */
+size_t tp_decode_packed_weight_bytes(int64_t K, int64_t N);
+int tp_decode_pack_weight(int dtype, int64_t K, int64_t N,
+                          const void *W, int64_t ldw,
+                          void *Wp, size_t wp_bytes, void *stream);
+int tp_decode_linear_packed(int act, int out_dtype, int64_t M, int64_t K, int64_t N,
+                            const void *X, int64_t ldx,
+                            const void *Wp, size_t wp_bytes,
+                            const void *bias,
+                            void *Y, int64_t ldy,
+                            void *ws, size_t ws_bytes, void *stream);
+size_t tp_decode_linear_packed_workspace(int64_t M, int64_t K, int64_t N);
+
+/*
  * Head-sharded self-attention block, this shard's partial output:
  *     [Q | K | V] = X @ Wqkv_i            (heads_local heads, each d wide)
  *     O_t = softmax(Q_t K_t^T / sqrt(d) [+ causal mask]) V_t   per head t

@@ -28,7 +28,8 @@ __all__ = [
     "tp_shard_sum", "tp_mlp_shard_backward", "tp_check_split", "tp_set_gemv_max_m",
     "tp_status_string", "tp_last_error", "tp_col_linear_gelu_workspace",
     "tp_row_linear_partial_workspace", "tp_attn_heads_shard_workspace",
-    "tp_mlp_shard_backward_workspace", "EXPORTED_SYMBOLS",
+    "tp_mlp_shard_backward_workspace", "tp_decode_packed_weight_bytes", "tp_decode_pack_weight",
+    "tp_decode_linear_packed", "tp_decode_linear_packed_workspace", "EXPORTED_SYMBOLS",
 ]
 
 TP_F32, TP_BF16 = 0, 1
@@ -50,6 +51,11 @@ _SIGS = {
     "tp_row_linear_partial": (_int, [_int, _i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                                      _vp, _sz, _vp]),
     "tp_row_linear_partial_workspace": (_sz, [_int, _i64, _i64, _i64]),
+    "tp_decode_packed_weight_bytes": (_sz, [_i64, _i64]),
+    "tp_decode_pack_weight": (_int, [_int, _i64, _i64, _vp, _i64, _vp, _sz, _vp]),
+    "tp_decode_linear_packed": (_int, [_int, _int, _i64, _i64, _i64, _vp, _i64, _vp, _sz, _vp, _vp, _i64,
+                                       _vp, _sz, _vp]),
+    "tp_decode_linear_packed_workspace": (_sz, [_i64, _i64, _i64]),
     "tp_attn_heads_shard": (_int, [_int, _i64, _i64, _i64, _i64, _i64, _int, _vp, _i64, _vp,
                                    _i64, _vp, _i64, _vp, _i64, _vp, _sz, _vp]),
     "tp_attn_heads_shard_workspace": (_sz, [_int, _i64, _i64, _i64, _i64]),
@@ -274,6 +280,41 @@ def tp_row_linear_partial(Xi, Wi, P, ws=None, stream=None):
     _check("tp_row_linear_partial", lib().tp_row_linear_partial(
         dt, M, Ki, N, px, ldx, pw, ldw, pp, ldp, pws, nws, _stream(stream, Xi)))
     return P
+
+
+def tp_decode_packed_weight_bytes(K, N) -> int:
+    return lib().tp_decode_packed_weight_bytes(K, N)
+
+
+def tp_decode_linear_packed_workspace(M, K, N) -> int:
+    return lib().tp_decode_linear_packed_workspace(M, K, N)
+
+
+def tp_decode_pack_weight(W, Wp=None, stream=None):
+    """The 64-column panel copy of the bf16 weight W [K x N] for
+    tp_decode_linear_packed; allocates Wp (uint8) unless one is given."""
+    pw, K, N, ldw = _mat(W, "W")
+    nbytes = tp_decode_packed_weight_bytes(K, N)
+    if Wp is None:
+        Wp = _torch().empty(nbytes, dtype=_torch().uint8, device=W.device)
+    _check("tp_decode_pack_weight", lib().tp_decode_pack_weight(
+        _dtype_code(W), K, N, pw, ldw, Wp.data_ptr(), Wp.numel() * Wp.element_size(), _stream(stream, W)))
+    return Wp
+
+
+def tp_decode_linear_packed(X, Wp, Y, act="gelu", bias=None, ws=None, stream=None):
+    """Y = act(X W + bias) from W's panels (Y bf16), or the float32 partial
+    Y = X W (Y float32, act 'none'); N is Y's width."""
+    a = _ACTS[act] if isinstance(act, str) else int(act)
+    px, M, K, ldx = _mat(X, "X")
+    py, _, N, ldy = _mat(Y, "Y")
+    need = tp_decode_linear_packed_workspace(M, K, N)
+    st = _stream(stream, X)
+    pws, nws = _workspace(ws, need, X.device, zeroed=True, stream=st)
+    _check("tp_decode_linear_packed", lib().tp_decode_linear_packed(
+        a, _dtype_code(Y), M, K, N, px, ldx, Wp.data_ptr(), Wp.numel() * Wp.element_size(), _ptr(bias),
+        py, ldy, pws, nws, st))
+    return Y
 
 
 def tp_attn_heads_shard(X, Wqkv, Wo, P, b, s, heads_local, d=128, causal=True, ws=None,

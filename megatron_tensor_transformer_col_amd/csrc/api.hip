@@ -567,6 +567,69 @@ int tp_row_linear_partial(int dtype, int64_t M, int64_t Ki, int64_t N, const voi
   return ok();
 }
 
+size_t tp_decode_packed_weight_bytes(int64_t K, int64_t N) {
+  if (K < 1 || N < 1 || K > kMaxDim || N > kMaxDim) return 0;
+  return gemv_packed_bytes(K, N);
+}
+
+int tp_decode_pack_weight(int dtype, int64_t K, int64_t N, const void *W, int64_t ldw, void *Wp,
+                          size_t wp_bytes, void *stream) {
+  if (dtype != TP_BF16) return fail(TP_ERR_DTYPE, "tp_decode_pack_weight: bf16 weights only");
+  TRY(check_dims({K, N}, "tp_decode_pack_weight"));
+  if (K < 1 || N < 1) return fail(TP_ERR_SHAPE, "K and N must be >= 1");
+  TRY(check_mat(W, K, N, ldw, 2, "W"));
+  if (Wp == nullptr) return fail(TP_ERR_ARG, "Wp is NULL");
+  if ((reinterpret_cast<uintptr_t>(Wp) & 15u) != 0) return fail(TP_ERR_ALIGN, "Wp is not 16-byte aligned");
+  const size_t need = gemv_packed_bytes(K, N);
+  if (wp_bytes < need) return fail(TP_ERR_SHAPE, "Wp holds %zu bytes, the panels need %zu", wp_bytes, need);
+  TRY(hip_status(launch_gemv_pack(static_cast<const uint16_t *>(W), ldw, K, N, static_cast<uint16_t *>(Wp),
+                                  static_cast<hipStream_t>(stream)),
+                 "decode weight pack"));
+  return ok();
+}
+
+size_t tp_decode_linear_packed_workspace(int64_t M, int64_t K, int64_t N) {
+  if (M < 1 || M > 16 || K < 1 || N < 1 || N > gemv_max_n()) return 0;
+  return gemv_workspace(K, N);
+}
+
+int tp_decode_linear_packed(int act, int out_dtype, int64_t M, int64_t K, int64_t N, const void *X, int64_t ldx,
+                            const void *Wp, size_t wp_bytes, const void *bias, void *Y, int64_t ldy, void *ws,
+                            size_t ws_bytes, void *stream) {
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU_ERF) return fail(TP_ERR_ARG, "activation %d", act);
+  if (out_dtype != TP_BF16 && out_dtype != TP_F32) return fail(TP_ERR_DTYPE, "output dtype %d", out_dtype);
+  if (out_dtype == TP_F32 && act != TP_ACT_NONE)
+    return fail(TP_ERR_ARG, "an fp32 output (a row-parallel partial) takes no activation");
+  TRY(check_dims({M, K, N}, "tp_decode_linear_packed"));
+  if (K < 1 || N < 1) return fail(TP_ERR_SHAPE, "K and N must be >= 1");
+  if (M > 16) return fail(TP_ERR_SHAPE, "the decode path takes at most 16 token rows, got %lld", (long long)M);
+  if (N > gemv_max_n()) return fail(TP_ERR_SHAPE, "N %lld exceeds the decode path's %lld", (long long)N,
+                                    (long long)gemv_max_n());
+  TRY(check_mat(X, M, K, ldx, 2, "X"));
+  TRY(check_mat(Y, M, N, ldy, out_dtype == TP_F32 ? 4 : 2, "Y"));
+  TRY(check_vec(bias, N, 2, "bias"));
+  if (Wp == nullptr) return fail(TP_ERR_ARG, "Wp is NULL");
+  if ((reinterpret_cast<uintptr_t>(Wp) & 15u) != 0) return fail(TP_ERR_ALIGN, "Wp is not 16-byte aligned");
+  if (wp_bytes < gemv_packed_bytes(K, N))
+    return fail(TP_ERR_SHAPE, "Wp holds %zu bytes, the panels of K %lld x N %lld take %zu", wp_bytes,
+                (long long)K, (long long)N, gemv_packed_bytes(K, N));
+  if (!gemv_fits(ldx, 64)) return fail(TP_ERR_SHAPE, "ldx %lld too large for the decode path", (long long)ldx);
+  if (M == 0) return ok();
+  const size_t need = gemv_workspace(K, N);
+  if (need > 0 && (ws == nullptr || ws_bytes < need))
+    return fail(TP_ERR_WORKSPACE, "decode path needs %zu workspace bytes, got %zu", need, ws_bytes);
+  if (ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(TP_ERR_ALIGN, "workspace is not 256-byte aligned");
+  GemvArgs g;
+  g.dtype = DT_BF16;
+  g.epi = out_dtype == TP_F32 ? EPI_STORE_F32 : (act == TP_ACT_GELU_ERF ? EPI_GELU : EPI_STORE);
+  g.M = M; g.K = K; g.N = N;
+  g.X = X; g.ldx = ldx; g.W = Wp; g.ldw = 0; g.packed = true;
+  g.bias = bias; g.Y = Y; g.ldy = ldy; g.ws = ws; g.ws_bytes = ws_bytes;
+  TRY(hip_status(launch_gemv(g, static_cast<hipStream_t>(stream)), "packed gemv"));
+  return ok();
+}
+
 int tp_attn_heads_shard(int dtype, int64_t b, int64_t s_len, int64_t h, int64_t heads_local,
                         int64_t d, int causal, const void *X, int64_t ldx, const void *Wqkv,
                         int64_t ldwqkv, const void *Wo, int64_t ldwo, float *P, int64_t ldp,

@@ -160,8 +160,8 @@ __device__ __forceinline__ void gv_fused_tail(const f32x4_t &acc, int M, int N, 
 template <int EPI, int OUT>
 __global__ void __launch_bounds__(GV_NT)
 gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const uint16_t *__restrict__ W,
-                    int64_t ldw, int K, int N, int krange, const uint16_t *bias, void *Y,
-                    int64_t ldy, float *part, int *cnt) {
+                    int64_t ldw, int64_t sstride, int ncl, int K, int N, int krange, const uint16_t *bias,
+                    void *Y, int64_t ldy, float *part, int *cnt) {
   constexpr bool FINAL = OUT == GV_FINAL;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[GV_STAGES * GV_STAGE + GV_XSLAB];
   uint16_t *xtail = smem + GV_STAGES * GV_STAGE;
@@ -188,13 +188,13 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   for (int j = 0; j < 2; ++j) {
     const int row = (wave + 4 * j) * 8 + (lane >> 3);
     const int lg = (lane & 7) ^ gv_swz(row);
-    const int colrel = min(n0 + lg * 8, N - 8) - n0;
+    const int colrel = min(n0 + lg * 8, ncl - 8) - n0;
     woff[j] = (uint32_t)(((int64_t)(lane >> 3) * ldw + colrel) * 2);
   }
   const int xrow = 4 * wave + ((lane >> 3) & 3);
   const uint32_t xoff_row = (uint32_t)((int64_t)min(xrow, M - 1) * ldx * 2);
   const uint32_t xoff = xoff_row + (uint32_t)(((lane & 7) ^ (xrow & 7)) * 16);
-  const uint16_t *Wn = W + n0;
+  const uint16_t *Wn = W + (int64_t)strip * sstride;  // this strip's column 0, row 0
   const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int s) {
     const int kr = k_begin + s * GV_SLAB;
@@ -314,21 +314,36 @@ gemv_finalize_kernel(const float *__restrict__ part, int splits, int M, int N,
   gv_finish<EPI>(sum, bias, col, Y, ldy, m);
 }
 
+// Where strip s of W starts and how its rows are laid out: row-major W
+// (strip origin 64 s, row stride ldw, columns clamped to N) or the panel
+// layout of gemv_pack_kernel (strip origin s * Kp * 64, row stride 64, every
+// column of a panel present).
+struct GvSrc {
+  int64_t ldw, sstride;
+  int ncl;
+};
+static GvSrc gv_src(const GemvArgs &a, const GvPlan &pl) {
+  if (a.packed) return GvSrc{GV_BN, gemv_panel_rows(a.K) * GV_BN, pl.strips * GV_BN};
+  return GvSrc{a.ldw, GV_BN, (int)a.N};
+}
+
 template <int EPI>
 static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
   const uint16_t *X = static_cast<const uint16_t *>(a.X);
   const uint16_t *W = static_cast<const uint16_t *>(a.W);
   const uint16_t *bias = static_cast<const uint16_t *>(a.bias);
+  const GvSrc src = gv_src(a, pl);
   const dim3 grid((unsigned)pl.strips, (unsigned)pl.splits);
   if (pl.splits == 1) {
     hipLaunchKernelGGL((gemv_partial_kernel<EPI, GV_FINAL>), grid, dim3(GV_NT), 0, s, X, a.ldx,
-                       (int)a.M, W, a.ldw, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy,
-                       (float *)nullptr, (int *)nullptr);
+                       (int)a.M, W, src.ldw, src.sstride, src.ncl, (int)a.K, (int)a.N, pl.krange, bias, a.Y,
+                       a.ldy, (float *)nullptr, (int *)nullptr);
     return hipGetLastError();
   }
   float *part = static_cast<float *>(a.ws);
   hipLaunchKernelGGL((gemv_partial_kernel<EPI, GV_PARTIAL>), grid, dim3(GV_NT), 0, s, X, a.ldx,
-                     (int)a.M, W, a.ldw, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy, part, (int *)nullptr);
+                     (int)a.M, W, src.ldw, src.sstride, src.ncl, (int)a.K, (int)a.N, pl.krange, bias, a.Y,
+                     a.ldy, part, (int *)nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = (int)a.M * (int)a.N;
@@ -339,10 +354,51 @@ static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
 
 bool gemv_fits(int64_t ldx, int64_t ldw) { return ldx <= GV_MAX_LD && ldw <= GV_MAX_LD; }
 
+// ---------------------------------------------------------------- panel layout
+// For decode, where the same weight is streamed once per generated token, a
+// weight can be stored once in the order the split-K pass reads it: panel s
+// holds columns 64 s .. 64 s + 63 of every row k < Kp (K rounded up to the
+// 64-row slab), 128 bytes per row, zeros past K and past N:
+//     Wp[(s * Kp + k) * 64 + c] = W[k][64 s + c]
+// A workgroup's K range of one strip is then one contiguous run of
+// krange * 128 bytes instead of 128 bytes from each of krange rows
+// ldw * 2 bytes apart, and every 1 KiB DMA op covers 8 whole rows of it.
+// The arithmetic (slabs, MFMA order, split order) is unchanged, so the
+// results equal the row-major path's bit for bit.
+int64_t gemv_panel_rows(int64_t K) { return (K + GV_SLAB - 1) / GV_SLAB * GV_SLAB; }
+
+size_t gemv_packed_bytes(int64_t K, int64_t N) {
+  return (size_t)((N + GV_BN - 1) / GV_BN) * (size_t)gemv_panel_rows(K) * GV_BN * sizeof(uint16_t);
+}
+
+// One thread per 16-byte granule of Wp (8 columns of one panel row).
+__global__ void __launch_bounds__(256)
+gemv_pack_kernel(const uint16_t *__restrict__ W, int64_t ldw, int K, int N, int64_t Kp, int64_t granules,
+                 uint16_t *__restrict__ Wp) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= granules) return;
+  const int64_t row = v >> 3;  // panel row over all panels: s * Kp + k
+  const int64_t s = row / Kp, k = row - s * Kp;
+  const int64_t col = s * GV_BN + (v & 7) * 8;
+  uint4 g = make_uint4(0u, 0u, 0u, 0u);
+  if (k < K && col < N) g = *reinterpret_cast<const uint4 *>(W + k * ldw + col);  // N % 8 == 0
+  reinterpret_cast<uint4 *>(Wp)[v] = g;
+}
+
+hipError_t launch_gemv_pack(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, uint16_t *Wp, hipStream_t s) {
+  if (K <= 0 || N <= 0) return hipSuccess;
+  if (N % 8 != 0 || ldw < N) return hipErrorInvalidValue;
+  const int64_t Kp = gemv_panel_rows(K);
+  const int64_t granules = (int64_t)gemv_packed_bytes(K, N) / 16;
+  hipLaunchKernelGGL(gemv_pack_kernel, dim3((unsigned)((granules + 255) / 256)), dim3(256), 0, s, W, ldw,
+                     (int)K, (int)N, Kp, granules, Wp);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
   if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8) return hipErrorInvalidValue;
-  if (!gemv_fits(a.ldx, a.ldw)) return hipErrorInvalidValue;
+  if (!gemv_fits(a.ldx, a.packed ? GV_BN : a.ldw)) return hipErrorInvalidValue;
   const GvPlan pl = gv_plan(a.K, a.N);
   if (pl.splits > 1 && (a.ws == nullptr || a.ws_bytes < gemv_workspace(a.K, a.N)))
     return hipErrorInvalidValue;
@@ -401,6 +457,7 @@ static unsigned char *noalloc_scratch(hipError_t *err) {
 
 hipError_t launch_gemv_noalloc(const GemvArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.packed) return hipErrorInvalidValue;  // row-major weights only
   if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8) return hipErrorInvalidValue;
   if (!gemv_fits(a.ldx, a.ldw) || !gemv_noalloc_fits(a.K, a.N)) return hipErrorInvalidValue;
   const GvPlan pl = gv_plan(a.K, a.N);
@@ -421,7 +478,7 @@ hipError_t launch_gemv_noalloc(const GemvArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)pl.strips, (unsigned)pl.splits);
 #define TP_GV_FUSED(E)                                                                                    \
   hipLaunchKernelGGL((gemv_partial_kernel<E, GV_FUSED>), grid, dim3(GV_NT), 0, s, X, a.ldx, (int)a.M, W,   \
-                     a.ldw, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy, part, cnt)
+                     a.ldw, (int64_t)GV_BN, (int)a.N, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy, part, cnt)
   switch (a.epi) {
     case EPI_GELU: TP_GV_FUSED(EPI_GELU); break;
     case EPI_STORE: TP_GV_FUSED(EPI_STORE); break;

@@ -86,8 +86,14 @@ struct GemvArgs {
   const void *bias = nullptr;
   void *Y = nullptr; int64_t ldy = 0;
   void *ws = nullptr; size_t ws_bytes = 0;
+  bool packed = false;  // W in the panel layout of launch_gemv_pack (ldw unused)
 };
-size_t gemv_workspace(int64_t K, int64_t N);
+size_t gemv_workspace(int64_t K, int64_t N);  // the same for both weight layouts
+// Panel layout for decode weights: Wp[(s * Kp + k) * 64 + c] = W[k][64 s + c]
+// (zeros past K and N), Kp = gemv_panel_rows(K).
+int64_t gemv_panel_rows(int64_t K);
+size_t gemv_packed_bytes(int64_t K, int64_t N);
+hipError_t launch_gemv_pack(const uint16_t *W, int64_t ldw, int64_t K, int64_t N, uint16_t *Wp, hipStream_t s);
 int64_t gemv_max_n();  // widest N the split-K decode path accepts
 bool gemv_fits(int64_t ldx, int64_t ldw);  // row strides the decode path's 32-bit offsets cover
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);

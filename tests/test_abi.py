@@ -286,3 +286,60 @@ def test_attention_backward_validation():
     assert call(fwn=fw - 256) == -5
     assert call(wsn=bw - 1) == -5
     assert call(ws=A + 16) == -3                   # workspace not 256-byte aligned
+
+
+def test_decode_packed_sizes():
+    """Panel bytes: ceil(N / 64) panels x (K rounded up to 64) rows x 64 bf16;
+    the packed GEMV's workspace is the row-major decode path's."""
+    assert tp.tp_decode_packed_weight_bytes(8192, 3584) == 56 * 8192 * 64 * 2
+    assert tp.tp_decode_packed_weight_bytes(1000, 200) == 4 * 1024 * 64 * 2
+    assert tp.tp_decode_packed_weight_bytes(0, 64) == 0
+    for K, N in [(8192, 3584), (3584, 8192), (1000, 200)]:
+        assert tp.tp_decode_linear_packed_workspace(16, K, N) == tp.tp_row_linear_partial_workspace(1, 16, K, N)
+    assert tp.tp_decode_linear_packed_workspace(17, 8192, 3584) == 0
+
+
+@host_only
+@pytest.mark.parametrize("case,expect", [
+    ("fp32", -4), ("null_wp", -1), ("misaligned_wp", -3), ("small_wp", -2), ("odd_width", -3), ("zero_k", -2)])
+def test_decode_pack_validation(case, expect):
+    lib = tp.lib()
+    a = dict(dt=1, K=1000, N=200, W=A, ldw=200, Wp=A, nwp=tp.tp_decode_packed_weight_bytes(1000, 200))
+    if case == "fp32": a["dt"] = 0
+    if case == "null_wp": a["Wp"] = None
+    if case == "misaligned_wp": a["Wp"] = MIS
+    if case == "small_wp": a["nwp"] -= 16
+    if case == "odd_width": a.update(N=196, ldw=200)
+    if case == "zero_k": a["K"] = 0
+    st = lib.tp_decode_pack_weight(a["dt"], a["K"], a["N"], a["W"], a["ldw"], a["Wp"], a["nwp"], None)
+    assert st == expect, tp.tp_last_error()
+    assert tp.tp_last_error()
+
+
+@host_only
+@pytest.mark.parametrize("case,expect", [
+    ("bad_act", -1), ("swiglu", -1), ("bad_out", -4), ("f32_gelu", -1), ("m17", -2), ("null_x", -1),
+    ("null_wp", -1), ("misaligned_wp", -3), ("small_wp", -2), ("no_ws", -5), ("misaligned_ws", -3),
+    ("ld_small", -2)])
+def test_decode_linear_packed_validation(case, expect):
+    lib = tp.lib()
+    K, N = 4096, 1024
+    a = dict(act=1, out=1, M=16, X=A, ldx=K, Wp=A, nwp=tp.tp_decode_packed_weight_bytes(K, N), bias=None,
+             Y=A, ldy=N, ws=A, nws=tp.tp_decode_linear_packed_workspace(16, K, N))
+    assert a["nws"] > 0
+    if case == "bad_act": a["act"] = 9
+    if case == "swiglu": a["act"] = 2
+    if case == "bad_out": a["out"] = 5
+    if case == "f32_gelu": a["out"] = 0
+    if case == "m17": a["M"] = 17
+    if case == "null_x": a["X"] = None
+    if case == "null_wp": a["Wp"] = None
+    if case == "misaligned_wp": a["Wp"] = MIS
+    if case == "small_wp": a["nwp"] -= 16
+    if case == "no_ws": a["ws"] = None
+    if case == "misaligned_ws": a["ws"] = A + 16
+    if case == "ld_small": a["ldy"] = N - 8
+    st = lib.tp_decode_linear_packed(a["act"], a["out"], a["M"], K, N, a["X"], a["ldx"], a["Wp"], a["nwp"],
+                                     a["bias"], a["Y"], a["ldy"], a["ws"], a["nws"], None)
+    assert st == expect, tp.tp_last_error()
+    assert tp.tp_last_error()
