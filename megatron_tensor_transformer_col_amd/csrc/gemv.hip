@@ -291,27 +291,49 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
 }
 
 // Y[m][c] = epi(sum_s part[s][m][c] + bias), splits added in order.  One
-// thread per output element, all of its (at most 16 per batch) partial loads
-// issued before the first add, so the kernel costs about one memory latency.
+// thread per 4 adjacent outputs of a token row (N is a multiple of 8, so a
+// group never straddles rows and every access is a 16- or 8-byte vector),
+// all of its (at most 16 per batch) partial loads issued before the first
+// add, so the kernel costs about one memory latency.  Per element the
+// arithmetic is gv_finish's, in the same order.
 template <int EPI>
 __global__ void __launch_bounds__(256)
 gemv_finalize_kernel(const float *__restrict__ part, int splits, int M, int N,
                      const uint16_t *bias, void *Y, int64_t ldy) {
   const int v = blockIdx.x * 256 + threadIdx.x;
-  if (v >= M * N) return;
-  const int m = v / N, col = v % N;
-  const float *p = part + (int64_t)m * N + col;
-  const int64_t step = (int64_t)16 * N;
-  float sum = 0.f;
+  const int n4 = N >> 2;
+  if (v >= M * n4) return;
+  const int m = v / n4, col = (v - m * n4) * 4;
+  const float4 *p = reinterpret_cast<const float4 *>(part + (int64_t)m * N + col);
+  const int64_t step = (int64_t)4 * N;  // float4s between splits
+  float sum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += 16) {
-    float t[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) t[j] = (s0 + j < splits) ? p[(int64_t)(s0 + j) * step] : 0.f;
+    float4 t[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j)
-      if (s0 + j < splits) sum += t[j];
+      t[j] = (s0 + j < splits) ? p[(int64_t)(s0 + j) * step] : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (s0 + j < splits) {
+        sum[0] += t[j].x; sum[1] += t[j].y; sum[2] += t[j].z; sum[3] += t[j].w;
+      }
   }
-  gv_finish<EPI>(sum, bias, col, Y, ldy, m);
+  if (bias != nullptr) {
+    const uint2 b = *reinterpret_cast<const uint2 *>(bias + col);
+    sum[0] += bf2f((uint16_t)(b.x & 0xffffu)); sum[1] += bf2f((uint16_t)(b.x >> 16));
+    sum[2] += bf2f((uint16_t)(b.y & 0xffffu)); sum[3] += bf2f((uint16_t)(b.y >> 16));
+  }
+  if constexpr (EPI == EPI_STORE_F32) {
+    *reinterpret_cast<float4 *>(static_cast<float *>(Y) + (int64_t)m * ldy + col) =
+        make_float4(sum[0], sum[1], sum[2], sum[3]);
+  } else {
+    if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum[r] = gelu_f(sum[r]);
+    }
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(Y) + (int64_t)m * ldy + col) =
+        make_uint2(pack_bf2(sum[0], sum[1]), pack_bf2(sum[2], sum[3]));
+  }
 }
 
 // Where strip s of W starts and how its rows are laid out: row-major W
@@ -346,7 +368,7 @@ static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
                      a.ldy, part, (int *)nullptr);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int total = (int)a.M * (int)a.N;
+  const int total = (int)a.M * (int)(a.N / 4);
   hipLaunchKernelGGL((gemv_finalize_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256),
                      0, s, part, pl.splits, (int)a.M, (int)a.N, bias, a.Y, a.ldy);
   return hipGetLastError();
@@ -397,7 +419,7 @@ hipError_t launch_gemv_pack(const uint16_t *W, int64_t ldw, int64_t K, int64_t N
 
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8) return hipErrorInvalidValue;
+  if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8 || a.N % 8 != 0) return hipErrorInvalidValue;
   if (!gemv_fits(a.ldx, a.packed ? GV_BN : a.ldw)) return hipErrorInvalidValue;
   const GvPlan pl = gv_plan(a.K, a.N);
   if (pl.splits > 1 && (a.ws == nullptr || a.ws_bytes < gemv_workspace(a.K, a.N)))
