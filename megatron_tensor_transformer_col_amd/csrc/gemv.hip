@@ -8,7 +8,9 @@
 //
 //  * Workgroup = 4 wave64 over a 64-column strip of W and one K range
 //    (split-K across workgroups so that a 3584 x 8192 or 8192 x 3584 shard
-//    spreads over all 256 CUs, two workgroups per CU).
+//    spreads over all 256 CUs, two workgroups per CU).  W is row-major, or
+//    packed once into 64-column panels (below), where a workgroup's share
+//    is one contiguous run instead of 128 bytes from each of its rows.
 //  * Each ring stage holds a 64-row slab of the strip (8 KiB) and the
 //    matching 16 x 64 slice of x (2 KiB); both move HBM -> LDS with
 //    global_load_lds_dwordx4 (no VGPR staging; the weights, read once per
