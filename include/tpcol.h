@@ -97,18 +97,15 @@ size_t tp_col_linear_gelu_workspace(int dtype, int act, int64_t M, int64_t K, in
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same
  * operation, arguments and results, with no workspace.  No call allocates.
  * The decode path (M <= the GEMV threshold) keeps its split-K partial sums
- * and per-strip arrival counters in a static device array of the library
- * (2 MiB of fp32 partials + 16384 counters, one copy per GPU, held until the
- * process ends) and finishes in one kernel: the workgroup that arrives last
- * on a 64-column strip adds the strip's partials in split order (the same
- * sums, in the same order, as tp_col_linear_gelu, so the results are
- * identical) and resets its counter.  Limit: the decode shape's partials,
- * splits * 16 * Ni * 4 bytes (tp_col_linear_gelu_workspace(), at most 2 MiB
- * for any K), must fit, and Ni <= 1048576 (one counter per 64-column strip),
- * else TP_ERR_SHAPE.  Larger M uses the GEMM path, which needs no
+ * in a static device array of the library (2 MiB of fp32 partials, one copy
+ * per GPU, held until the process ends) and runs the same two kernels as
+ * tp_col_linear_gelu (the split-K pass, then the sum of the partials in
+ * split order with bias and activation), so the results are identical.
+ * Every decode shape fits that array (the split count is chosen so that the
+ * partials never exceed 2 MiB).  Larger M uses the GEMM path, which needs no
  * scratch.  Calls that overlap on one GPU (different streams, or different
- * host threads without ordering) share the array and race; calls ordered on
- * one stream do not.
+ * host threads without ordering) share the array and race; calls ordered
+ * on one stream do not.
  */
 int tp_col_linear_gelu_noalloc(int dtype, int act, int64_t M, int64_t K, int64_t Ni,
                                const void *X, int64_t ldx,

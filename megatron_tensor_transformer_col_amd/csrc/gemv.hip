@@ -86,84 +86,14 @@ __device__ __forceinline__ int gv_swz(int r) { return (((r >> 1) & 1) | (((r >> 
 // How a workgroup's 16 x 64 result leaves the kernel.
 enum GvOut {
   GV_FINAL = 0,   // single split: bias + activation applied here
-  GV_PARTIAL = 1, // fp32 partial to part[split]; gemv_finalize_kernel adds them
-  GV_FUSED = 2    // fp32 partial to part[split], then the workgroup that
-                  // arrives last on its strip (arrival counter cnt[strip])
-                  // adds the strip's partials in split order and finishes
+  GV_PARTIAL = 1  // fp32 partial to part[split]; gemv_finalize_kernel adds them
 };
-
-// Sum of the strip's partials in split order + bias + activation, then the
-// store: the same arithmetic, in the same order, as gemv_finalize_kernel.
-template <int EPI>
-__device__ __forceinline__ void gv_finish(float sum, const uint16_t *bias, int col, void *Y, int64_t ldy, int m) {
-  if (bias != nullptr) sum += bf2f(bias[col]);
-  if constexpr (EPI == EPI_STORE_F32) {
-    static_cast<float *>(Y)[(int64_t)m * ldy + col] = sum;
-  } else {
-    if constexpr (EPI == EPI_GELU) sum = gelu_f(sum);
-    static_cast<uint16_t *>(Y)[(int64_t)m * ldy + col] = f2bf(sum);
-  }
-}
-
-// GV_FUSED tail, called by every thread of the workgroup (the kernel's
-// early return for lanes outside M / N comes after it): the partial goes out with device-scope
-// (agent) relaxed atomic stores, which are coherent across the XCDs' L2s;
-// once they have completed (vmcnt 0) and every wave has passed the barrier,
-// one thread bumps the strip's arrival counter.  The workgroup that sees
-// splits - 1 resets the counter for the next call and reads the strip's
-// partials with device-scope loads.  No workgroup ever waits for another.
-template <int EPI>
-__device__ __forceinline__ void gv_fused_tail(const f32x4_t &acc, int M, int N, int splits, int n0, int split,
-                                              int cw, const uint16_t *bias, void *Y, int64_t ldy, float *part,
-                                              int *cnt) {
-  __shared__ int s_last;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int g = lane >> 4, m = lane & 15;
-  const int col = n0 + cw + 4 * g;
-  if (m < M && col < N) {
-    float *pp = part + ((int64_t)split * 16 + m) * N + col;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) __hip_atomic_store(pp + r, acc[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(cnt + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = old == splits - 1;
-    if (last) __hip_atomic_store(cnt + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = last;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // 16 x 64 outputs of the strip, four per thread
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int v = tid + q * GV_NT;
-    const int mm = v >> 6, c = n0 + (v & 63);
-    if (mm >= M || c >= N) continue;
-    const float *p = part + (int64_t)mm * N + c;
-    const int64_t step = (int64_t)16 * N;
-    float sum = 0.f;
-    for (int s0 = 0; s0 < splits; s0 += 8) {
-      float t[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        t[j] = (s0 + j < splits) ? __hip_atomic_load(p + (int64_t)(s0 + j) * step, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT)
-                                 : 0.f;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if (s0 + j < splits) sum += t[j];
-    }
-    gv_finish<EPI>(sum, bias, c, Y, ldy, mm);
-  }
-}
 
 template <int EPI, int OUT>
 __global__ void __launch_bounds__(GV_NT)
 gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const uint16_t *__restrict__ W,
                     int64_t ldw, int64_t sstride, int ncl, int K, int N, int krange, const uint16_t *bias,
-                    void *Y, int64_t ldy, float *part, int *cnt) {
+                    void *Y, int64_t ldy, float *part) {
   constexpr bool FINAL = OUT == GV_FINAL;
   __shared__ __attribute__((aligned(1024))) uint16_t smem[GV_STAGES * GV_STAGE + GV_XSLAB];
   uint16_t *xtail = smem + GV_STAGES * GV_STAGE;
@@ -261,10 +191,6 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
   }
 
   // ---- this wave's 16 x 16 result: lane holds [m = l16][cw + 4g + r]
-  if constexpr (OUT == GV_FUSED) {
-    gv_fused_tail<EPI>(acc, M, N, (int)gridDim.y, n0, split, cw, bias, Y, ldy, part, cnt);
-    return;
-  }
   const int m = l16;
   const int col = n0 + cw + 4 * g;
   if (m >= M || col >= N) return;
@@ -296,8 +222,7 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
 // thread per 4 adjacent outputs of a token row (N is a multiple of 8, so a
 // group never straddles rows and every access is a 16- or 8-byte vector),
 // all of its (at most 16 per batch) partial loads issued before the first
-// add, so the kernel costs about one memory latency.  Per element the
-// arithmetic is gv_finish's, in the same order.
+// add, so the kernel costs about one memory latency.
 template <int EPI>
 __global__ void __launch_bounds__(256)
 gemv_finalize_kernel(const float *__restrict__ part, int splits, int M, int N,
@@ -361,13 +286,13 @@ static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
   if (pl.splits == 1) {
     hipLaunchKernelGGL((gemv_partial_kernel<EPI, GV_FINAL>), grid, dim3(GV_NT), 0, s, X, a.ldx,
                        (int)a.M, W, src.ldw, src.sstride, src.ncl, (int)a.K, (int)a.N, pl.krange, bias, a.Y,
-                       a.ldy, (float *)nullptr, (int *)nullptr);
+                       a.ldy, (float *)nullptr);
     return hipGetLastError();
   }
   float *part = static_cast<float *>(a.ws);
   hipLaunchKernelGGL((gemv_partial_kernel<EPI, GV_PARTIAL>), grid, dim3(GV_NT), 0, s, X, a.ldx,
                      (int)a.M, W, src.ldw, src.sstride, src.ncl, (int)a.K, (int)a.N, pl.krange, bias, a.Y,
-                     a.ldy, part, (int *)nullptr);
+                     a.ldy, part);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = (int)a.M * (int)(a.N / 4);
@@ -436,23 +361,20 @@ hipError_t launch_gemv(const GemvArgs &a, hipStream_t s) {
 
 // ---------------------------------------------------------------- allocation-free variant
 // For callers that cannot allocate (graph capture, serving loops): the
-// split-K partials and the per-strip arrival counters live in this
-// file-scope device array instead of a caller workspace.  Static device
-// memory starts zeroed, and every call leaves the counters it used at zero
-// (the last workgroup of each strip resets its own), so nothing is cleared
-// per call.  Each GPU holds its own copy until the process ends; calls that
-// overlap on one GPU share it and race.
-static constexpr size_t NA_PART_BYTES = (size_t)2 << 20;  // fp32 partials [splits][16][N]; splits * N <= 512 * 64
-static constexpr int NA_MAX_STRIPS = 16384;               // arrival counters (N <= 1M columns)
-static constexpr size_t NA_BYTES = NA_PART_BYTES + (size_t)NA_MAX_STRIPS * sizeof(int);
-static __device__ __align__(256) unsigned char scratch[NA_BYTES];
+// split-K partials live in this file-scope device array instead of a caller
+// workspace, and the same two kernels run (split-K pass, then the finalize
+// that adds the partials in split order), so the results are those of
+// launch_gemv bit for bit.  Every partial a call reads was written by that
+// call's split-K pass, so nothing is cleared.  Each GPU holds its own copy
+// until the process ends; calls that overlap on one GPU share it and race.
+// Any decode shape fits: the plan keeps splits * strips <= GV_TARGET_WG, so
+// the partials (splits * 16 * N fp32) take at most 512 * 64 * 16 * 4 bytes.
+static constexpr size_t NA_PART_BYTES = (size_t)GV_TARGET_WG * GV_BN * 16 * sizeof(float);  // 2 MiB
+static __device__ __align__(256) unsigned char scratch[NA_PART_BYTES];
 
 size_t gemv_noalloc_max_bytes() { return NA_PART_BYTES; }
 
-bool gemv_noalloc_fits(int64_t K, int64_t N) {
-  const GvPlan pl = gv_plan(K, N);
-  return pl.strips <= NA_MAX_STRIPS && gemv_workspace(K, N) <= NA_PART_BYTES;
-}
+bool gemv_noalloc_fits(int64_t K, int64_t N) { return gemv_workspace(K, N) <= NA_PART_BYTES; }
 
 namespace {
 std::mutex g_na_mu;
@@ -481,36 +403,18 @@ static unsigned char *noalloc_scratch(hipError_t *err) {
 
 hipError_t launch_gemv_noalloc(const GemvArgs &a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (a.packed) return hipErrorInvalidValue;  // row-major weights only
-  if (a.M > 16 || a.dtype != DT_BF16 || a.K < 1 || a.N < 8) return hipErrorInvalidValue;
-  if (!gemv_fits(a.ldx, a.ldw) || !gemv_noalloc_fits(a.K, a.N)) return hipErrorInvalidValue;
-  const GvPlan pl = gv_plan(a.K, a.N);
-  if (pl.splits == 1) {
-    GemvArgs b = a;
-    b.ws = nullptr;
-    b.ws_bytes = 0;
-    return launch_gemv(b, s);
+  if (a.packed || !gemv_noalloc_fits(a.K, a.N)) return hipErrorInvalidValue;
+  GemvArgs b = a;
+  b.ws = nullptr;
+  b.ws_bytes = 0;
+  if (gv_plan(a.K, a.N).splits > 1) {
+    hipError_t e = hipSuccess;
+    unsigned char *base = noalloc_scratch(&e);
+    if (base == nullptr) return e;
+    b.ws = base;
+    b.ws_bytes = NA_PART_BYTES;
   }
-  hipError_t e = hipSuccess;
-  unsigned char *base = noalloc_scratch(&e);
-  if (base == nullptr) return e;
-  float *part = reinterpret_cast<float *>(base);
-  int *cnt = reinterpret_cast<int *>(base + NA_PART_BYTES);
-  const uint16_t *X = static_cast<const uint16_t *>(a.X);
-  const uint16_t *W = static_cast<const uint16_t *>(a.W);
-  const uint16_t *bias = static_cast<const uint16_t *>(a.bias);
-  const dim3 grid((unsigned)pl.strips, (unsigned)pl.splits);
-#define TP_GV_FUSED(E)                                                                                    \
-  hipLaunchKernelGGL((gemv_partial_kernel<E, GV_FUSED>), grid, dim3(GV_NT), 0, s, X, a.ldx, (int)a.M, W,   \
-                     a.ldw, (int64_t)GV_BN, (int)a.N, (int)a.K, (int)a.N, pl.krange, bias, a.Y, a.ldy, part, cnt)
-  switch (a.epi) {
-    case EPI_GELU: TP_GV_FUSED(EPI_GELU); break;
-    case EPI_STORE: TP_GV_FUSED(EPI_STORE); break;
-    case EPI_STORE_F32: TP_GV_FUSED(EPI_STORE_F32); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef TP_GV_FUSED
-  return hipGetLastError();
+  return launch_gemv(b, s);
 }
 
 }  // namespace tpcol

@@ -97,9 +97,9 @@ hipError_t launch_gemv_pack(const uint16_t *W, int64_t ldw, int64_t K, int64_t N
 int64_t gemv_max_n();  // widest N the split-K decode path accepts
 bool gemv_fits(int64_t ldx, int64_t ldw);  // row strides the decode path's 32-bit offsets cover
 hipError_t launch_gemv(const GemvArgs &a, hipStream_t s);
-// The same with the split-K partials and arrival counters in the library's
-// static scratch (no workspace; one kernel).  gemv_noalloc_fits: the shape's
-// partials fit that scratch (gemv_noalloc_max_bytes()).
+// The same with the split-K partials in the library's static scratch (no
+// workspace; the same two kernels).  gemv_noalloc_fits: the shape's partials
+// fit that scratch (gemv_noalloc_max_bytes(); true for every decode shape).
 hipError_t launch_gemv_noalloc(const GemvArgs &a, hipStream_t s);
 bool gemv_noalloc_fits(int64_t K, int64_t N);
 size_t gemv_noalloc_max_bytes();

@@ -2,8 +2,9 @@
 tp_col_linear_gelu on the GPU.  Both compute the same sums in the same order
 (the decode path's split-K partials are added in split order either way), so
 their outputs must be bitwise equal.  Each case runs two calls in a row, the
-second on a smaller input, and the decode cases repeat, so that arrival
-counters left non-zero by a call would show up in the next one."""
+second on a smaller input, and the decode cases repeat, so that partials a
+call left in the library's static scratch would show up in the next one if
+any were read without being rewritten."""
 import pytest
 
 from gpu_util import note, torch
