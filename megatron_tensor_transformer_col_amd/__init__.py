@@ -306,6 +306,8 @@ def tp_decode_linear_packed(X, Wp, Y, act="gelu", bias=None, ws=None, stream=Non
     """Y = act(X W + bias) from W's panels (Y bf16), or the float32 partial
     Y = X W (Y float32, act 'none'); N is Y's width."""
     a = _ACTS[act] if isinstance(act, str) else int(act)
+    if _dtype_code(X) != TP_BF16:
+        raise TypeError("tp_decode_linear_packed takes a bfloat16 X")
     px, M, K, ldx = _mat(X, "X")
     py, _, N, ldy = _mat(Y, "Y")
     need = tp_decode_linear_packed_workspace(M, K, N)

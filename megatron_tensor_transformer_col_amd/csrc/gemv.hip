@@ -339,6 +339,7 @@ hipError_t launch_gemv_pack(const uint16_t *W, int64_t ldw, int64_t K, int64_t N
   if (N % 8 != 0 || ldw < N) return hipErrorInvalidValue;
   const int64_t Kp = gemv_panel_rows(K);
   const int64_t granules = (int64_t)gemv_packed_bytes(K, N) / 16;
+  if ((granules + 255) / 256 > (int64_t)0x7fffffff) return hipErrorInvalidValue;  // one grid dimension
   hipLaunchKernelGGL(gemv_pack_kernel, dim3((unsigned)((granules + 255) / 256)), dim3(256), 0, s, W, ldw,
                      (int)K, (int)N, Kp, granules, Wp);
   return hipGetLastError();
