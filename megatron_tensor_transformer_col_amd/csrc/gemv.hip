@@ -222,12 +222,15 @@ gemv_partial_kernel(const uint16_t *__restrict__ X, int64_t ldx, int M, const ui
 // thread per 4 adjacent outputs of a token row (N is a multiple of 8, so a
 // group never straddles rows and every access is a 16- or 8-byte vector),
 // all of its (at most 16 per batch) partial loads issued before the first
-// add, so the kernel costs about one memory latency.
+// add, so the kernel costs about one memory latency.  One wave per
+// workgroup spreads those loads over as many CUs as there are waves (224 for
+// a 16 x 3584 output, against 56 with 256-thread workgroups: 14.30 -> 14.10
+// us per packed column GEMV, interleaved on one box).
 template <int EPI>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(64)
 gemv_finalize_kernel(const float *__restrict__ part, int splits, int M, int N,
                      const uint16_t *bias, void *Y, int64_t ldy) {
-  const int v = blockIdx.x * 256 + threadIdx.x;
+  const int v = blockIdx.x * 64 + threadIdx.x;
   const int n4 = N >> 2;
   if (v >= M * n4) return;
   const int m = v / n4, col = (v - m * n4) * 4;
@@ -296,7 +299,7 @@ static hipError_t run_gemv(const GemvArgs &a, const GvPlan &pl, hipStream_t s) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int total = (int)a.M * (int)(a.N / 4);
-  hipLaunchKernelGGL((gemv_finalize_kernel<EPI>), dim3((unsigned)((total + 255) / 256)), dim3(256),
+  hipLaunchKernelGGL((gemv_finalize_kernel<EPI>), dim3((unsigned)((total + 63) / 64)), dim3(64),
                      0, s, part, pl.splits, (int)a.M, (int)a.N, bias, a.Y, a.ldy);
   return hipGetLastError();
 }
